@@ -1,0 +1,721 @@
+// Host side of the DBSA library: argument checks, planning, workspace layout,
+// per-call table staging and kernel launches behind the C ABI in dbsa.h.
+//
+// Method: "Efficient Many-Shot In-Context Learning with Dynamic Block-Sparse
+// Attention" (paper-notes page, ACL 2025), cited as [Notes, section].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "dbsa.h"
+#include "dbsa_internal.hpp"
+
+namespace dbsa {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DBSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Argument checks (pure host code, no HIP calls).
+// ---------------------------------------------------------------------------
+int check_attn(const dbsa_attn_t* a) {
+  if (!a) return fail(DBSA_EINVAL, "attn is NULL");
+  if (a->n_q_heads < 1 || a->n_kv_heads < 1)
+    return fail(DBSA_EINVAL, "head counts must be >= 1 (got %d q, %d kv)", a->n_q_heads,
+                a->n_kv_heads);
+  if (a->n_q_heads % a->n_kv_heads != 0)
+    return fail(DBSA_EUNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                a->n_q_heads, a->n_kv_heads);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(DBSA_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", a->head_dim);
+  if (a->dtype != DBSA_BF16 && a->dtype != DBSA_F32)
+    return fail(DBSA_EUNSUPPORTED, "dtype %d not supported", a->dtype);
+  if (!(a->rope_theta > 0.0) || !std::isfinite(a->rope_theta))
+    return fail(DBSA_EINVAL, "rope_theta must be finite and > 0");
+  if (!std::isfinite(a->softmax_scale)) return fail(DBSA_EINVAL, "softmax_scale not finite");
+  return DBSA_OK;
+}
+
+// Block offsets [Notes, Method > Stage 1, item 1]; also checks the blocks.
+int check_blocks(const dbsa_blocks_t* b, std::vector<int32_t>& off) {
+  if (!b) return fail(DBSA_EINVAL, "blocks is NULL");
+  if (b->n_blocks < 1) return fail(DBSA_EINVAL, "n_blocks must be >= 1 (got %d)", b->n_blocks);
+  if (!b->block_lens) return fail(DBSA_EINVAL, "block_lens is NULL");
+  if (b->sink != 0 && b->sink != 1) return fail(DBSA_EINVAL, "sink must be 0 or 1");
+  if (b->j < 0) return fail(DBSA_EINVAL, "j must be >= 0 (got %d)", b->j);
+  off.assign((size_t)b->n_blocks + 1, 0);
+  int64_t total = 0;
+  for (int i = 0; i < b->n_blocks; ++i) {
+    if (b->block_lens[i] < 1)
+      return fail(DBSA_EINVAL, "block %d has length %d (must be >= 1)", i, b->block_lens[i]);
+    total += b->block_lens[i];
+    if (total >= (int64_t(1) << 31) - 1024)
+      return fail(DBSA_EINVAL, "pool too long (>= 2^31 tokens)");
+    off[i + 1] = (int32_t)total;
+  }
+  return DBSA_OK;
+}
+
+// Selected ids [Notes, Method > Stage 2, items 1-2]: anchor first, distinct, in range.
+int check_ids(const int32_t* ids, int32_t n_ids, int32_t batch, int32_t n_blocks) {
+  if (!ids) return fail(DBSA_EINVAL, "ids is NULL");
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_ids < 1) return fail(DBSA_EINVAL, "n_ids must be >= 1");
+  std::vector<char> seen((size_t)n_blocks);
+  for (int b = 0; b < batch; ++b) {
+    std::fill(seen.begin(), seen.end(), 0);
+    const int32_t* row = ids + (int64_t)b * n_ids;
+    if (row[0] != 0)
+      return fail(DBSA_EINVAL, "ids row %d starts with %d: the anchor block 0 must come first", b,
+                  row[0]);
+    for (int i = 0; i < n_ids; ++i) {
+      if (row[i] < 0 || row[i] >= n_blocks)
+        return fail(DBSA_EINVAL, "ids[%d][%d] = %d out of range [0, %d)", b, i, row[i], n_blocks);
+      if (seen[row[i]]) return fail(DBSA_EINVAL, "ids row %d repeats block %d", b, row[i]);
+      seen[row[i]] = 1;
+    }
+  }
+  return DBSA_OK;
+}
+
+RopeFreq make_freq(const dbsa_attn_t* a) {
+  RopeFreq f;
+  const int half = a->head_dim / 2;
+  for (int i = 0; i < kMaxHalf; ++i)
+    f.rev[i] = i < half ? std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI) : 0.0;
+  return f;
+}
+
+float q_scale_of(const dbsa_attn_t* a) {
+  const double s = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0 / std::sqrt((double)a->head_dim);
+  return (float)(s * 1.4426950408889634);
+}
+
+size_t elem_bytes(const dbsa_attn_t* a) { return a->dtype == DBSA_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Pinned staging ring: per-call tables go host -> device by an async copy on
+// the caller's stream from a slot that is reused only after its copy is done.
+// ---------------------------------------------------------------------------
+constexpr int kSlots = 16;
+constexpr size_t kSlotBytes = size_t(1) << 20;
+
+struct Ring {
+  std::mutex mu;
+  char* host = nullptr;
+  hipEvent_t ev[kSlots] = {};
+  bool pending[kSlots] = {};
+  int next = 0;
+};
+
+std::mutex g_rings_mu;
+std::map<int, Ring*> g_rings;
+
+int stage_bytes(const void* src, size_t n, void* dst, hipStream_t s) {
+  if (n == 0) return DBSA_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  Ring* r;
+  {
+    std::lock_guard<std::mutex> g(g_rings_mu);
+    Ring*& slot = g_rings[dev];
+    if (!slot) {
+      Ring* nr = new Ring();
+      e = hipHostMalloc(reinterpret_cast<void**>(&nr->host), kSlots * kSlotBytes,
+                        hipHostMallocDefault);
+      if (e != hipSuccess) {
+        delete nr;
+        return hip_fail(e, "hipHostMalloc(staging ring)");
+      }
+      for (int i = 0; i < kSlots; ++i) {
+        e = hipEventCreateWithFlags(&nr->ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+      }
+      slot = nr;
+    }
+    r = slot;
+  }
+  std::lock_guard<std::mutex> g(r->mu);
+  const int k = r->next;
+  r->next = (k + 1) % kSlots;
+  if (r->pending[k]) {
+    e = hipEventSynchronize(r->ev[k]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging slot)");
+  }
+  char* h = r->host + (size_t)k * kSlotBytes;
+  std::memcpy(h, src, n);
+  e = hipMemcpyAsync(dst, h, n, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
+  e = hipEventRecord(r->ev[k], s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  r->pending[k] = true;
+  return DBSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1 planning.
+// ---------------------------------------------------------------------------
+struct Stage1Plan {
+  std::vector<int32_t> off;  // offsets of all blocks (incl. an appended block)
+  int32_t n_tokens = 0;      // keys available (pool + appended block)
+  int32_t row0 = 0, row1 = 0;
+  int32_t sink_tiles = 0, win_tile0 = 0, win_tile1 = 0, n_slots = 0;
+  // workspace layout
+  size_t off_meta = 0, off_k = 0, off_v = 0, total = 0;
+  size_t meta_bytes = 0;
+};
+
+// Key tiles a set of rows can see: the window [lo, end) of the rows' block
+// plus the anchor; for a whole-pool prefill that is every tile.
+void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sink, int j) {
+  const int nb = (int)p.off.size() - 1;
+  if (whole_pool) {
+    p.sink_tiles = 0;
+    p.win_tile0 = 0;
+  } else {
+    // rows are the last block (index nb - 1)
+    const int lo = p.off[std::max(nb - 1 - j, 0)];
+    p.win_tile0 = lo / kKeyTile;
+    p.sink_tiles = (sink && lo > 0) ? std::min<int>((int)cdiv(p.off[1], kKeyTile), p.win_tile0) : 0;
+  }
+  p.win_tile1 = (int32_t)cdiv(p.n_tokens, kKeyTile);
+  p.n_slots = p.sink_tiles + (p.win_tile1 - p.win_tile0);
+  p.meta_bytes = p.off.size() * sizeof(int32_t);
+  p.off_meta = 0;
+  size_t cur = align_up(p.meta_bytes);
+  if (a->dtype == DBSA_BF16) {
+    const size_t tile = (size_t)kKeyTile * a->head_dim * 2;
+    p.off_k = cur;
+    cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
+    p.off_v = cur;
+    cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
+  }
+  p.total = cur;
+}
+
+int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Plan& p,
+                  const void* q, int32_t q_row0, const void* k, const void* v, void* o,
+                  void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  int rc = stage_bytes(p.off.data(), p.meta_bytes, w + p.off_meta, s);
+  if (rc) return rc;
+  const RopeFreq freq = make_freq(a);
+  PrefillArgs pa;
+  pa.q = q;
+  pa.o = o;
+  pa.offsets = reinterpret_cast<const int32_t*>(w + p.off_meta);
+  pa.n_blocks = (int32_t)p.off.size() - 1;
+  pa.sink = blk->sink;
+  pa.j = blk->j;
+  pa.row0 = p.row0;
+  pa.row1 = p.row1;
+  pa.q_row0 = q_row0;
+  pa.hq = a->n_q_heads;
+  pa.hkv = a->n_kv_heads;
+  pa.n_qtiles = (int32_t)cdiv(p.row1 - p.row0, kPrefillRows);
+  pa.sink_tiles = p.sink_tiles;
+  pa.win_tile0 = p.win_tile0;
+  pa.n_slots = p.n_slots;
+  pa.q_scale = q_scale_of(a);
+  pa.freq = freq;
+  if (a->dtype == DBSA_BF16) {
+    PackArgs ka;
+    ka.k = k;
+    ka.v = v;
+    ka.k_tiles = w + p.off_k;
+    ka.v_tiles = w + p.off_v;
+    ka.n_tokens = p.n_tokens;
+    ka.hkv = a->n_kv_heads;
+    ka.sink_tiles = p.sink_tiles;
+    ka.win_tile0 = p.win_tile0;
+    ka.win_tile1 = p.win_tile1;
+    ka.n_slots = p.n_slots;
+    ka.freq = freq;
+    hipError_t e = launch_pack(ka, a->head_dim, a->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "launch k_pack");
+    pa.k_tiles = ka.k_tiles;
+    pa.v_tiles = ka.v_tiles;
+  } else {
+    pa.k_tiles = k;  // f32 rows kernel reads the unrotated pool directly
+    pa.v_tiles = v;
+  }
+  hipError_t e = launch_prefill(pa, a->head_dim, a->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launch prefill");
+  return DBSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2 planning.
+// ---------------------------------------------------------------------------
+struct SegPlan {
+  std::vector<int32_t> tables;  // start | src | buf | nseg | pos0 | dst_row
+  int32_t stride = 0;
+  size_t o_start = 0, o_src = 0, o_buf = 0, o_nseg = 0, o_pos0 = 0, o_dst = 0;  // int32 index
+};
+
+struct QueryPlan {
+  int32_t rows = 0, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
+};
+
+void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max_ctx,
+                 QueryPlan& qp) {
+  const int G = a->n_q_heads / a->n_kv_heads;
+  qp.rows = n_new * G;
+  qp.row_groups = (int32_t)cdiv(qp.rows, 256);
+  const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
+  qp.n_split = 1;
+  qp.tiles_per_split = (int32_t)n_tiles;
+  if (a->dtype == DBSA_BF16) {
+    const int64_t base = (int64_t)batch * a->n_kv_heads * qp.row_groups;
+    const int64_t want = std::max<int64_t>(1, cdiv(512, base));
+    const int64_t by_len = std::max<int64_t>(1, n_tiles / 4);
+    const int64_t ns = std::min(want, by_len);
+    qp.tiles_per_split = (int32_t)cdiv(n_tiles, ns);
+    qp.n_split = (int32_t)cdiv(n_tiles, qp.tiles_per_split);
+  }
+}
+
+void query_layout(const dbsa_attn_t* a, int32_t batch, size_t meta_ints, QueryPlan& qp) {
+  qp.meta_bytes = meta_ints * sizeof(int32_t);
+  qp.off_meta = 0;
+  size_t cur = align_up(qp.meta_bytes);
+  if (qp.n_split > 1) {
+    const size_t prow = (size_t)batch * a->n_kv_heads * qp.n_split * qp.rows;
+    qp.off_po = cur;
+    cur = align_up(cur + prow * a->head_dim * sizeof(float));
+    qp.off_ml = cur;
+    cur = align_up(cur + prow * 2 * sizeof(float));
+  }
+  qp.total = cur;
+}
+
+size_t seg_meta_ints(int32_t batch, int32_t stride) {
+  return (size_t)batch * stride * 3 + (size_t)batch * 3;
+}
+
+void seg_init(SegPlan& sp, int32_t batch, int32_t stride) {
+  sp.stride = stride;
+  sp.tables.assign(seg_meta_ints(batch, stride), 0);
+  sp.o_start = 0;
+  sp.o_src = (size_t)batch * stride;
+  sp.o_buf = 2 * (size_t)batch * stride;
+  sp.o_nseg = 3 * (size_t)batch * stride;
+  sp.o_pos0 = sp.o_nseg + batch;
+  sp.o_dst = sp.o_pos0 + batch;
+}
+
+int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const void* q,
+                      const void* k_new, const void* v_new, const void* k_pool,
+                      const void* v_pool, void* k_buf, void* v_buf, int64_t cap, void* o,
+                      const SegPlan& sp, const QueryPlan& qp, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  int rc = stage_bytes(sp.tables.data(), qp.meta_bytes, w + qp.off_meta, s);
+  if (rc) return rc;
+  const int32_t* dt = reinterpret_cast<const int32_t*>(w + qp.off_meta);
+  const RopeFreq freq = make_freq(a);
+
+  NewKVArgs na;
+  na.k_new = k_new;
+  na.v_new = v_new;
+  na.k_dst = k_buf;
+  na.v_dst = v_buf;
+  na.dst_row = dt + sp.o_dst;
+  na.pos0 = dt + sp.o_pos0;
+  na.n_new = n_new;
+  na.hkv = a->n_kv_heads;
+  na.cap = cap;
+  na.freq = freq;
+  hipError_t e = launch_new_kv(na, batch, a->head_dim, a->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launch new_kv");
+
+  QueryArgs qa;
+  qa.q = q;
+  qa.k_pool = k_pool;
+  qa.v_pool = v_pool;
+  qa.k_ctx = k_buf;
+  qa.v_ctx = v_buf;
+  qa.o = o;
+  qa.part_o = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_po) : nullptr;
+  qa.part_ml = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_ml) : nullptr;
+  qa.seg.start = dt + sp.o_start;
+  qa.seg.src = dt + sp.o_src;
+  qa.seg.buf = dt + sp.o_buf;
+  qa.seg.nseg = dt + sp.o_nseg;
+  qa.seg.seg_stride = sp.stride;
+  qa.pos0 = dt + sp.o_pos0;
+  qa.n_new = n_new;
+  qa.hq = a->n_q_heads;
+  qa.hkv = a->n_kv_heads;
+  qa.rows = qp.rows;
+  qa.row_groups = qp.row_groups;
+  qa.n_split = qp.n_split;
+  qa.tiles_per_split = qp.tiles_per_split;
+  qa.cap = cap;
+  qa.q_scale = q_scale_of(a);
+  qa.freq = freq;
+  e = launch_query(qa, batch, a->head_dim, a->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launch query");
+  if (qp.n_split > 1) {
+    CombineArgs ca;
+    ca.part_o = qa.part_o;
+    ca.part_ml = qa.part_ml;
+    ca.o = o;
+    ca.n_new = n_new;
+    ca.hq = a->n_q_heads;
+    ca.hkv = a->n_kv_heads;
+    ca.rows = qp.rows;
+    ca.n_split = qp.n_split;
+    e = launch_combine(ca, batch, a->head_dim, a->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "launch combine");
+  }
+  return DBSA_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DBSA_OK;
+  if (!ws) return fail(DBSA_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(DBSA_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(DBSA_ENOSPC, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  return DBSA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps, const char* names) {
+  for (const void* p : ps)
+    if (!p) return fail(DBSA_EINVAL, "NULL tensor pointer among (%s)", names);
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) % 16)
+      return fail(DBSA_EINVAL, "tensor pointers must be 16-byte aligned (%s)", names);
+  return DBSA_OK;
+}
+
+int check_meta(size_t bytes) {
+  if (bytes > kSlotBytes)
+    return fail(DBSA_EUNSUPPORTED, "per-call tables of %zu bytes exceed the %zu-byte limit",
+                bytes, kSlotBytes);
+  return DBSA_OK;
+}
+
+// Plans shared by the entry points and dbsa_workspace_bytes.
+int plan_prefill(const dbsa_attn_t* a, const dbsa_blocks_t* b, Stage1Plan& p) {
+  int rc = check_attn(a);
+  if (!rc) rc = check_blocks(b, p.off);
+  if (rc) return rc;
+  p.n_tokens = p.off.back();
+  p.row0 = 0;
+  p.row1 = p.n_tokens;
+  stage1_layout(a, p, true, b->sink, b->j);
+  return check_meta(p.meta_bytes);
+}
+
+int plan_append(const dbsa_attn_t* a, const dbsa_blocks_t* b, int64_t new_len, Stage1Plan& p) {
+  int rc = check_attn(a);
+  if (!rc) rc = check_blocks(b, p.off);
+  if (rc) return rc;
+  if (new_len < 1) return fail(DBSA_EINVAL, "new_len must be >= 1");
+  const int64_t n_old = p.off.back();
+  if (n_old + new_len >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "pool too long");
+  p.off.push_back((int32_t)(n_old + new_len));
+  p.n_tokens = (int32_t)(n_old + new_len);
+  p.row0 = (int32_t)n_old;
+  p.row1 = p.n_tokens;
+  stage1_layout(a, p, false, b->sink, b->j);
+  return check_meta(p.meta_bytes);
+}
+
+int plan_gather(const dbsa_attn_t* a, const dbsa_blocks_t* b, const int32_t* ids, int32_t n_ids,
+                int32_t batch, std::vector<int32_t>* tables, std::vector<int64_t>* lens,
+                size_t* meta_bytes) {
+  std::vector<int32_t> off;
+  int rc = check_attn(a);
+  if (!rc) rc = check_blocks(b, off);
+  if (rc) return rc;
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_ids < 1) return fail(DBSA_EINVAL, "n_ids must be >= 1");
+  *meta_bytes = (size_t)batch * (2 * n_ids + 1) * sizeof(int32_t);
+  rc = check_meta(*meta_bytes);
+  if (rc || !ids) return rc;
+  rc = check_ids(ids, n_ids, batch, b->n_blocks);
+  if (rc) return rc;
+  if (tables) {
+    tables->assign((size_t)batch * (2 * n_ids + 1), 0);
+    int32_t* st = tables->data();
+    int32_t* src = st + (size_t)batch * (n_ids + 1);
+    lens->assign(batch, 0);
+    for (int r = 0; r < batch; ++r) {
+      int64_t pos = 0;
+      for (int i = 0; i < n_ids; ++i) {
+        const int blkid = ids[(int64_t)r * n_ids + i];
+        st[(int64_t)r * (n_ids + 1) + i] = (int32_t)pos;
+        src[(int64_t)r * n_ids + i] = off[blkid];
+        pos += off[blkid + 1] - off[blkid];
+      }
+      st[(int64_t)r * (n_ids + 1) + n_ids] = (int32_t)pos;
+      (*lens)[r] = pos;
+    }
+  }
+  return DBSA_OK;
+}
+
+}  // namespace
+}  // namespace dbsa
+
+using namespace dbsa;
+
+extern "C" {
+
+const char* dbsa_last_error(void) { return g_err; }
+
+const char* dbsa_version(void) { return "dbsa-gfx950 0.1.0"; }
+
+size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                            int64_t rows, int32_t batch, int32_t n_ids, int64_t max_ctx) {
+  g_err[0] = 0;
+  switch (op) {
+    case DBSA_OP_PREFILL: {
+      Stage1Plan p;
+      return plan_prefill(attn, blocks, p) ? 0 : p.total;
+    }
+    case DBSA_OP_APPEND: {
+      Stage1Plan p;
+      return plan_append(attn, blocks, rows, p) ? 0 : p.total;
+    }
+    case DBSA_OP_GATHER: {
+      size_t mb = 0;
+      if (plan_gather(attn, blocks, nullptr, n_ids, batch, nullptr, nullptr, &mb)) return 0;
+      return align_up(mb);
+    }
+    case DBSA_OP_QUERY:
+    case DBSA_OP_QUERY_GATHERED: {
+      if (check_attn(attn)) return 0;
+      if (batch < 1 || rows < 1 || max_ctx < rows || max_ctx >= (int64_t(1) << 31)) {
+        fail(DBSA_EINVAL, "need batch >= 1, n_new >= 1 and n_new <= max_ctx < 2^31");
+        return 0;
+      }
+      if (op == DBSA_OP_QUERY_GATHERED && n_ids < 1) {
+        fail(DBSA_EINVAL, "n_ids must be >= 1");
+        return 0;
+      }
+      const int32_t stride = op == DBSA_OP_QUERY ? 2 : n_ids + 2;
+      QueryPlan qp;
+      query_split(attn, batch, (int32_t)rows, max_ctx, qp);
+      query_layout(attn, batch, seg_meta_ints(batch, stride), qp);
+      if (check_meta(qp.meta_bytes)) return 0;
+      return qp.total;
+    }
+    default:
+      fail(DBSA_EINVAL, "unknown op %d", op);
+      return 0;
+  }
+}
+
+int dbsa_prefill(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const void* q,
+                 const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                 void* stream) {
+  g_err[0] = 0;
+  Stage1Plan p;
+  int rc = plan_prefill(attn, blocks, p);
+  if (!rc) rc = check_ptrs({q, k, v, o}, "q, k, v, o");
+  if (!rc) rc = check_ws(ws, ws_bytes, p.total);
+  if (rc) return rc;
+  return launch_stage1(attn, blocks, p, q, 0, k, v, o, ws, static_cast<hipStream_t>(stream));
+}
+
+int dbsa_append_block(const dbsa_attn_t* attn, const dbsa_blocks_t* existing, int32_t new_len,
+                      const void* q_new, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, int64_t cache_capacity_tokens, void* o_new, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  Stage1Plan p;
+  int rc = plan_append(attn, existing, new_len, p);
+  if (!rc) rc = check_ptrs({q_new, k_new, v_new, k_cache, v_cache, o_new},
+                           "q_new, k_new, v_new, k_cache, v_cache, o_new");
+  if (!rc && p.n_tokens > cache_capacity_tokens)
+    rc = fail(DBSA_ENOSPC, "cache holds %lld tokens, %d needed", (long long)cache_capacity_tokens,
+              p.n_tokens);
+  if (!rc) rc = check_ws(ws, ws_bytes, p.total);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The new block's K/V join the unrotated cache [Notes, Method > Stage 1, items 3-4].
+  const size_t row_bytes = (size_t)attn->n_kv_heads * attn->head_dim * elem_bytes(attn);
+  char* kc = static_cast<char*>(k_cache) + (size_t)p.row0 * row_bytes;
+  char* vc = static_cast<char*>(v_cache) + (size_t)p.row0 * row_bytes;
+  hipError_t e = hipMemcpyAsync(kc, k_new, (size_t)new_len * row_bytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(vc, v_new, (size_t)new_len * row_bytes, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(append K/V)");
+  return launch_stage1(attn, existing, p, q_new, p.row0, k_cache, v_cache, o_new, ws, s);
+}
+
+int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const int32_t* ids,
+                     int32_t n_ids, int32_t batch, const void* k_pool, const void* v_pool,
+                     void* k_out, void* v_out, int64_t out_capacity_tokens, int64_t* ctx_len_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<int32_t> tables;
+  std::vector<int64_t> lens;
+  size_t mb = 0;
+  int rc = plan_gather(attn, blocks, ids, n_ids, batch, &tables, &lens, &mb);
+  if (!rc && !ids) rc = fail(DBSA_EINVAL, "ids is NULL");
+  if (!rc) rc = check_ptrs({k_pool, v_pool, k_out, v_out}, "k_pool, v_pool, k_out, v_out");
+  if (!rc && !ctx_len_out) rc = fail(DBSA_EINVAL, "ctx_len_out is NULL");
+  int64_t max_len = 0;
+  if (!rc) {
+    for (int64_t L : lens) max_len = std::max(max_len, L);
+    if (max_len > out_capacity_tokens)
+      rc = fail(DBSA_ENOSPC, "gathered context of %lld tokens exceeds out_capacity_tokens %lld",
+                (long long)max_len, (long long)out_capacity_tokens);
+  }
+  if (!rc) rc = check_ws(ws, ws_bytes, align_up(mb));
+  if (rc) return rc;
+  for (int r = 0; r < batch; ++r) ctx_len_out[r] = lens[r];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = stage_bytes(tables.data(), mb, ws, s);
+  if (rc) return rc;
+  GatherArgs ga;
+  ga.k_pool = k_pool;
+  ga.v_pool = v_pool;
+  ga.k_out = k_out;
+  ga.v_out = v_out;
+  ga.start = static_cast<const int32_t*>(ws);
+  ga.src = ga.start + (size_t)batch * (n_ids + 1);
+  ga.n_ids = n_ids;
+  ga.hkv = attn->n_kv_heads;
+  ga.cap = out_capacity_tokens;
+  ga.max_len = (int32_t)max_len;
+  ga.freq = make_freq(attn);
+  hipError_t e = launch_gather(ga, batch, attn->head_dim, attn->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launch gather");
+  return DBSA_OK;
+}
+
+int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const void* q,
+                    const void* k_new, const void* v_new, void* k_ctx, void* v_ctx,
+                    const int64_t* ctx_len, int64_t ctx_capacity, void* o, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_attn(attn);
+  if (rc) return rc;
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_new < 0) return fail(DBSA_EINVAL, "n_new must be >= 0");
+  if (n_new == 0) return DBSA_OK;  // nothing to attend
+  if (!ctx_len) return fail(DBSA_EINVAL, "ctx_len is NULL");
+  rc = check_ptrs({q, k_new, v_new, k_ctx, v_ctx, o}, "q, k_new, v_new, k_ctx, v_ctx, o");
+  if (rc) return rc;
+  int64_t max_ctx = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (ctx_len[b] < 0) return fail(DBSA_EINVAL, "ctx_len[%d] < 0", b);
+    if (ctx_len[b] + n_new > ctx_capacity)
+      return fail(DBSA_ENOSPC, "ctx_len[%d] + n_new = %lld exceeds ctx_capacity %lld", b,
+                  (long long)(ctx_len[b] + n_new), (long long)ctx_capacity);
+    max_ctx = std::max(max_ctx, ctx_len[b] + n_new);
+  }
+  if (max_ctx >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
+  QueryPlan qp;
+  query_split(attn, batch, n_new, max_ctx, qp);
+  SegPlan sp;
+  seg_init(sp, batch, 2);
+  query_layout(attn, batch, sp.tables.size(), qp);
+  rc = check_meta(qp.meta_bytes);
+  if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
+  if (rc) return rc;
+  for (int b = 0; b < batch; ++b) {
+    int32_t* t = sp.tables.data();
+    t[sp.o_start + (size_t)b * 2 + 0] = 0;
+    t[sp.o_start + (size_t)b * 2 + 1] = (int32_t)(ctx_len[b] + n_new);
+    t[sp.o_src + (size_t)b * 2] = 0;
+    t[sp.o_buf + (size_t)b * 2] = 1;
+    t[sp.o_nseg + b] = 1;
+    t[sp.o_pos0 + b] = (int32_t)ctx_len[b];
+    t[sp.o_dst + b] = (int32_t)ctx_len[b];
+  }
+  return launch_query_path(attn, batch, n_new, q, k_new, v_new, nullptr, nullptr, k_ctx, v_ctx,
+                           ctx_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
+}
+
+int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                             const int32_t* ids, int32_t n_ids, int32_t batch,
+                             const void* k_pool, const void* v_pool, int32_t n_new,
+                             const void* q, const void* k_new, const void* v_new, void* k_tail,
+                             void* v_tail, const int64_t* tail_len, int64_t tail_capacity,
+                             void* o, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<int32_t> off;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_blocks(blocks, off);
+  if (rc) return rc;
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_new < 0) return fail(DBSA_EINVAL, "n_new must be >= 0");
+  rc = check_ids(ids, n_ids, batch, blocks->n_blocks);
+  if (rc) return rc;
+  if (n_new == 0) return DBSA_OK;
+  if (!tail_len) return fail(DBSA_EINVAL, "tail_len is NULL");
+  rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
+                  "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
+  if (rc) return rc;
+  const int32_t stride = n_ids + 2;
+  SegPlan sp;
+  seg_init(sp, batch, stride);
+  int64_t max_ctx = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (tail_len[b] < 0) return fail(DBSA_EINVAL, "tail_len[%d] < 0", b);
+    if (tail_len[b] + n_new > tail_capacity)
+      return fail(DBSA_ENOSPC, "tail_len[%d] + n_new = %lld exceeds tail_capacity %lld", b,
+                  (long long)(tail_len[b] + n_new), (long long)tail_capacity);
+    int32_t* t = sp.tables.data();
+    int64_t pos = 0;
+    for (int i = 0; i < n_ids; ++i) {
+      const int blkid = ids[(int64_t)b * n_ids + i];
+      t[sp.o_start + (size_t)b * stride + i] = (int32_t)pos;
+      t[sp.o_src + (size_t)b * stride + i] = off[blkid];
+      t[sp.o_buf + (size_t)b * stride + i] = 0;
+      pos += off[blkid + 1] - off[blkid];
+    }
+    const int64_t total = pos + tail_len[b] + n_new;
+    if (total >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
+    t[sp.o_start + (size_t)b * stride + n_ids] = (int32_t)pos;  // tail segment
+    t[sp.o_src + (size_t)b * stride + n_ids] = 0;
+    t[sp.o_buf + (size_t)b * stride + n_ids] = 1;
+    t[sp.o_start + (size_t)b * stride + n_ids + 1] = (int32_t)total;
+    t[sp.o_nseg + b] = n_ids + 1;
+    t[sp.o_pos0 + b] = (int32_t)(pos + tail_len[b]);
+    t[sp.o_dst + b] = (int32_t)tail_len[b];
+    max_ctx = std::max(max_ctx, total);
+  }
+  QueryPlan qp;
+  query_split(attn, batch, n_new, max_ctx, qp);
+  query_layout(attn, batch, sp.tables.size(), qp);
+  rc = check_meta(qp.meta_bytes);
+  if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
+  if (rc) return rc;
+  return launch_query_path(attn, batch, n_new, q, k_new, v_new, k_pool, v_pool, k_tail, v_tail,
+                           tail_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

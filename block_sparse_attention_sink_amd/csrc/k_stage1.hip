@@ -1,0 +1,369 @@
+// Stage 1 of DBSA on gfx950: block-sparse streaming prefill.
+//
+// [Notes, Method > Stage 1]: block i attends to the anchor block (sink), to the
+// previous j blocks and causally to itself; tokens sit at sequential
+// positions; K/V are kept unrotated.  The page's implementation skips masked
+// blocks; here the skipping is by construction: each 128-row query tile walks
+// only the 64-key tiles that meet its visible key intervals.
+//
+// Kernels
+//   k_pack_bf16     rotate K once per key tile and transpose V, writing each
+//                   tile as the exact LDS byte image the prefill consumes.
+//   k_prefill_bf16  flash attention on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
+//                   S^T = K Q^T and O^T += V^T P^T so that every softmax row
+//                   statistic lives in one lane pair; online softmax in exp2.
+//   k_rows_f32      one wavefront per (row, head) in float32 for the f32
+//                   dtype (no MFMA; small correctness-grade problems).
+#include "dbsa_device.hpp"
+
+namespace dbsa {
+
+// ---------------------------------------------------------------------------
+// K rotation + V transpose into tile images.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
+  constexpr int CP = D / 16;  // chunk pairs per key row (first half / second half)
+  constexpr int CR = D / 8;   // 16-byte chunks per key row
+  constexpr int NT = 64 * CP;
+  __shared__ __align__(16) uint16_t vs[64][D + 8];
+
+  const int slot = blockIdx.x, g = blockIdx.y;
+  const int kt = slot < a.sink_tiles ? slot : a.win_tile0 + (slot - a.sink_tiles);
+  const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
+  const int64_t tok = (int64_t)kt * kKeyTile + key;
+
+  u32x4 k1 = u32x4{0u, 0u, 0u, 0u}, k2 = k1, v1 = k1, v2 = k1;
+  if (tok < a.n_tokens) {
+    const int64_t row = (tok * a.hkv + g) * D;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + row);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + row);
+    k1 = kp[c];
+    k2 = kp[c + CP];
+    v1 = vp[c];
+    v2 = vp[c + CP];
+    rope_rotate_chunk(k1, k2, tok, a.freq, 8 * c);
+  }
+  const int64_t tile = (int64_t)g * a.n_slots + slot;
+  u32x4* ko = reinterpret_cast<u32x4*>(a.k_tiles) + tile * (64 * CR);
+  ko[key * CR + k_chunk_phys<D>(key, c)] = k1;
+  ko[key * CR + k_chunk_phys<D>(key, c + CP)] = k2;
+
+  *reinterpret_cast<u32x4*>(&vs[key][8 * c]) = v1;
+  *reinterpret_cast<u32x4*>(&vs[key][D / 2 + 8 * c]) = v2;
+  __syncthreads();
+
+  u32x4* vo = reinterpret_cast<u32x4*>(a.v_tiles) + tile * (D * 8);
+  for (int u = tid; u < D * 8; u += NT) {
+    const int drow = u >> 3, ch = u & 7;
+    const int kbase = 16 * (ch >> 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) {
+      const int p = 8 * (ch & 1) + r;
+      const uint32_t lo = vs[kbase + vt_key_of_pos(p)][drow];
+      const uint32_t hi = vs[kbase + vt_key_of_pos(p + 1)][drow];
+      w[r >> 1] = lo | (hi << 16);
+    }
+    vo[drow * 8 + vt_chunk_phys(drow, ch)] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse flash prefill, bf16 in / bf16 out, fp32 accumulation.
+//
+// Workgroup = 4 wavefronts = 128 query rows of one query head; wave w owns
+// rows r0 + 32w .. +31, lane l holds row (l % 32) and, in its half h = l / 32,
+// half of every 64-key tile's scores for that row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_prefill_bf16(PrefillArgs a) {
+  constexpr int KS = D / 16;          // MFMA k-steps over the head dim
+  constexpr int OT = D / 32;          // 32-row O^T tiles
+  constexpr int CR = D / 8;           // 16-byte chunks per K row
+  constexpr int TU4 = 64 * D / 8;     // u32x4 per tile matrix
+  constexpr int PER_T = TU4 / 256;    // u32x4 per thread per matrix
+  __shared__ u32x4 lds[2][2][TU4];    // [stage][K, V^T]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, col = lane & 31;
+
+  // Logical work item: (kv head g, query tile qt, query head within the group).
+  const int G = a.hq / a.hkv;
+  const int lam = xcd_logical(blockIdx.x, gridDim.x);
+  const int per_g = a.n_qtiles * G;
+  const int g = lam / per_g;
+  const int rem = lam - g * per_g;
+  const int qt = rem / G;
+  const int head = g * G + (rem - qt * G);
+  const int r0 = a.row0 + qt * kPrefillRows;
+  const int r1 = min(r0 + kPrefillRows, a.row1);
+  const int t = r0 + wave * kRowsPerWave + col;
+
+  // Visible key intervals [Notes, Method > Stage 1, item 2]:
+  // row t sees [lo(t), t] with lo(t) = start of block max(blk(t) - j, 0),
+  // plus the anchor block [0, sink_end) when the sink is on.
+  const int32_t* off = a.offsets;
+  const int nb = a.n_blocks;
+  const int sink_end = a.sink ? off[1] : 0;
+  const int lo_t = off[max(upper_index(off, nb, min(t, r1 - 1)) - a.j, 0)];
+  const int lo_first = off[max(upper_index(off, nb, r0) - a.j, 0)];
+  const int lo_last = off[max(upper_index(off, nb, r1 - 1) - a.j, 0)];
+  const int win0 = lo_first / kKeyTile;
+  const int win1 = (r1 + kKeyTile - 1) / kKeyTile;
+  int nsink = 0;
+  if (a.sink && lo_last > 0) nsink = min((sink_end + kKeyTile - 1) / kKeyTile, win0);
+  const int n_tiles = nsink + (win1 - win0);
+
+  // Q: rotate at position t, fold scale * log2(e), round once to bf16.
+  bf16x8 qb[KS];
+  {
+    u32x4 raw[KS];
+    const bool live = t < r1;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)(t - a.q_row0) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], t, a.freq, 16 * ks + 8 * hh, a.q_scale);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+
+  f32x16 oacc[OT];
+#pragma unroll
+  for (int m = 0; m < OT; ++m) oacc[m] = f32x16{};
+  float m_run = kMaxFloor, l_run = 0.0f;
+
+  const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * TU4;
+  const u32x4* vbase = reinterpret_cast<const u32x4*>(a.v_tiles) + (int64_t)g * a.n_slots * TU4;
+  auto tile_of = [&](int it) { return it < nsink ? it : win0 + (it - nsink); };
+  auto slot_of = [&](int kt) {
+    return kt < a.sink_tiles ? kt : a.sink_tiles + (kt - a.win_tile0);
+  };
+
+  u32x4 kreg[PER_T], vreg[PER_T];
+  {
+    const int64_t s0 = (int64_t)slot_of(tile_of(0)) * TU4;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      lds[0][0][tid + 256 * i] = kbase[s0 + tid + 256 * i];
+      lds[0][1][tid + 256 * i] = vbase[s0 + tid + 256 * i];
+    }
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int cur = it & 1;
+    const int kt = tile_of(it);
+    if (it + 1 < n_tiles) {
+      const int64_t sn = (int64_t)slot_of(tile_of(it + 1)) * TU4;
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        kreg[i] = kbase[sn + tid + 256 * i];
+        vreg[i] = vbase[sn + tid + 256 * i];
+      }
+    }
+    const u32x4* Kl = lds[cur][0];
+    const u32x4* Vl = lds[cur][1];
+
+    // S^T (keys x rows) for the two 32-key halves of the tile.
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ka0 =
+          __builtin_bit_cast(bf16x8, Kl[col * CR + k_chunk_phys<D>(col, 2 * ks + hh)]);
+      const bf16x8 ka1 = __builtin_bit_cast(
+          bf16x8, Kl[(32 + col) * CR + k_chunk_phys<D>(32 + col, 2 * ks + hh)]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
+    }
+
+    // Element mask only on tiles some row cannot fully see.
+    const int k0 = kt * kKeyTile;
+    const bool full = (k0 + kKeyTile - 1 <= r0) &&
+                      (k0 >= lo_last || (a.sink && k0 + kKeyTile <= sink_end));
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = (i >> 2) * 8 + hh * 4 + (i & 3);
+        const int sa = k0 + kr, sb = k0 + 32 + kr;
+        const bool va = sa <= t && (sa >= lo_t || sa < sink_end);
+        const bool vb = sb <= t && (sb >= lo_t || sb < sink_end);
+        s0[i] = va ? s0[i] : kNegInf;
+        s1[i] = vb ? s1[i] : kNegInf;
+      }
+    }
+
+    // Online softmax (base 2; scores already carry scale * log2 e).
+    float mx = kMaxFloor;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = __builtin_amdgcn_exp2f(s0[i] - m_new);
+      s1[i] = __builtin_amdgcn_exp2f(s1[i] - m_new);
+      rs += s0[i] + s1[i];
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int m = 0; m < OT; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
+
+    // P^T as the B operand: k-step kk covers keys 16kk .. 16kk+15.
+    bf16x8 pb[4];
+    pb[0] = pack_p<0>(s0);
+    pb[1] = pack_p<8>(s0);
+    pb[2] = pack_p<0>(s1);
+    pb[3] = pack_p<8>(s1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int m = 0; m < OT; ++m) {
+        const int drow = m * 32 + col;
+        const bf16x8 va =
+            __builtin_bit_cast(bf16x8, Vl[drow * 8 + vt_chunk_phys(drow, 2 * kk + hh)]);
+        oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], oacc[m], 0, 0, 0);
+      }
+
+    if (it + 1 < n_tiles) {
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        lds[cur ^ 1][0][tid + 256 * i] = kreg[i];
+        lds[cur ^ 1][1][tid + 256 * i] = vreg[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (t < r1) {
+    const float inv = 1.0f / l_run;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + ((int64_t)(t - a.q_row0) * a.hq + head) * D;
+#pragma unroll
+    for (int m = 0; m < OT; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = m * 32 + q4 * 8 + hh * 4;
+        const u32x2 w = {pack_bf16x2(oacc[m][4 * q4 + 0] * inv, oacc[m][4 * q4 + 1] * inv),
+                         pack_bf16x2(oacc[m][4 * q4 + 2] * inv, oacc[m][4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 prefill: one wavefront per (row, head), one key per lane.
+// k / v are the unrotated f32 pool; keys are rotated on the fly.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void rows_f32_chunk(const float (&qr)[D], const float* k,
+                                               const float* v, int64_t key_stride,
+                                               int s0, int s1, float& m_run, float& l_run,
+                                               float (&acc)[2], const RopeFreq& f, int lane) {
+  constexpr int H = D / 2;
+  for (int base = s0; base < s1; base += 64) {
+    const int s = base + lane;
+    float sc = kNegInf;
+    if (s < s1) {
+      const float* kr = k + (int64_t)s * key_stride;
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        float c, sn;
+        rope_cs(s, f.rev[i], c, sn);
+        const float x1 = kr[i], x2 = kr[i + H];
+        dot += qr[i] * rot_lo(x1, x2, c, sn) + qr[i + H] * rot_hi(x1, x2, c, sn);
+      }
+      sc = dot;
+    }
+    float mx = sc;
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float p = __builtin_amdgcn_exp2f(sc - m_new);
+    float ps = p;
+    for (int o = 32; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    acc[0] *= alpha;
+    acc[1] *= alpha;
+    const int n = min(64, s1 - base);
+    for (int kk = 0; kk < n; ++kk) {
+      const float pk = __shfl(p, kk);
+      const float* vr = v + (int64_t)(base + kk) * key_stride;
+      if (lane < D) acc[0] += pk * vr[lane];
+      if (lane + 64 < D) acc[1] += pk * vr[lane + 64];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_rows_f32(PrefillArgs a) {
+  constexpr int H = D / 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = a.row0 + blockIdx.x * 4 + wave;
+  const int head = blockIdx.y;
+  if (t >= a.row1) return;  // no block-level synchronisation below
+  const int g = head / (a.hq / a.hkv);
+  const float* q = static_cast<const float*>(a.q) + ((int64_t)(t - a.q_row0) * a.hq + head) * D;
+  float qr[D];
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    float c, s;
+    rope_cs(t, a.freq.rev[i], c, s);
+    qr[i] = rot_lo(q[i], q[i + H], c, s) * a.q_scale;
+    qr[i + H] = rot_hi(q[i], q[i + H], c, s) * a.q_scale;
+  }
+  const int32_t* off = a.offsets;
+  const int sink_end = a.sink ? off[1] : 0;
+  const int lo_t = off[max(upper_index(off, a.n_blocks, t) - a.j, 0)];
+  const float* k = static_cast<const float*>(a.k_tiles) + (int64_t)g * D;
+  const float* v = static_cast<const float*>(a.v_tiles) + (int64_t)g * D;
+  const int64_t stride = (int64_t)a.hkv * D;
+  float m_run = kMaxFloor, l_run = 0.0f, acc[2] = {0.0f, 0.0f};
+  if (a.sink && lo_t > 0) rows_f32_chunk<D>(qr, k, v, stride, 0, sink_end, m_run, l_run, acc, a.freq, lane);
+  rows_f32_chunk<D>(qr, k, v, stride, lo_t, t + 1, m_run, l_run, acc, a.freq, lane);
+  float* o = static_cast<float*>(a.o) + ((int64_t)(t - a.q_row0) * a.hq + head) * D;
+  if (lane < D) o[lane] = acc[0] / l_run;
+  if (lane + 64 < D) o[lane + 64] = acc[1] / l_run;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_pack(const PackArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  (void)dtype;
+  const dim3 grid(a.n_slots, a.hkv);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(k_pack_bf16<128>, grid, dim3(64 * 8), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_pack_bf16<64>, grid, dim3(64 * 4), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  if (dtype == 1) {  // float32
+    const dim3 grid((a.row1 - a.row0 + 3) / 4, a.hq);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(k_rows_f32<128>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_rows_f32<64>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(a.n_qtiles * a.hq);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(k_prefill_bf16<128>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_prefill_bf16<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dbsa

@@ -1,0 +1,317 @@
+"""Python binding of libdbsa.so (argument marshalling only).
+
+Every function passes torch tensors' device pointers and the current HIP
+stream to the C ABI declared in include/dbsa.h; all computation happens in the
+library's gfx950 kernels.  If the library is missing, calls raise: there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "DbsaError", "load", "dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope",
+    "dbsa_query_attn", "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_version",
+    "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so")
+
+OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+OP_PREFILL, OP_APPEND, OP_GATHER, OP_QUERY, OP_QUERY_GATHERED = 0, 1, 2, 3, 4
+SYMBOLS = ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
+           "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_last_error", "dbsa_version")
+
+
+class DbsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dbsa error {code}: {msg}")
+        self.code = code
+
+
+class AttnT(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+
+
+class BlocksT(ctypes.Structure):
+    _fields_ = [("block_lens", ctypes.POINTER(ctypes.c_int32)), ("n_blocks", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("j", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdbsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise DbsaError(EHIP, f"{LIB_PATH} not built (run python -m "
+                              "block_sparse_attention_sink_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pa, pb = ctypes.POINTER(AttnT), ctypes.POINTER(BlocksT)
+    p32, p64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.dbsa_prefill.argtypes = [pa, pb, vp, vp, vp, vp, vp, sz, vp]
+    lib.dbsa_append_block.argtypes = [pa, pb, i32, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.dbsa_gather_rope.argtypes = [pa, pb, p32, i32, i32, vp, vp, vp, vp, i64, p64, vp, sz, vp]
+    lib.dbsa_query_attn.argtypes = [pa, i32, i32, vp, vp, vp, vp, vp, p64, i64, vp, vp, sz, vp]
+    lib.dbsa_query_attn_gathered.argtypes = [pa, pb, p32, i32, i32, vp, vp, i32, vp, vp, vp, vp,
+                                             vp, p64, i64, vp, vp, sz, vp]
+    lib.dbsa_workspace_bytes.argtypes = [ctypes.c_int, pa, pb, i64, i32, i32, i64]
+    lib.dbsa_workspace_bytes.restype = sz
+    lib.dbsa_last_error.restype = ctypes.c_char_p
+    lib.dbsa_version.restype = ctypes.c_char_p
+    for name in ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
+                 "dbsa_query_attn_gathered"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def dbsa_version() -> str:
+    return load().dbsa_version().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise DbsaError(rc, load().dbsa_last_error().decode())
+
+
+def attn_t(n_q_heads, n_kv_heads, head_dim, dtype, theta, scale=None) -> AttnT:
+    return AttnT(n_q_heads, n_kv_heads, head_dim, dtype, float(theta),
+                 0.0 if scale is None else float(scale))
+
+
+class Blocks:
+    """Keeps the host block_lens array alive for the call."""
+
+    def __init__(self, block_lens, sink: int, j: int):
+        self.lens = np.ascontiguousarray(np.asarray(block_lens, dtype=np.int32))
+        self.t = BlocksT(self.lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         int(self.lens.size), int(sink), int(j))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise DbsaError(EUNSUPPORTED, f"dtype {t.dtype} not supported (bfloat16 or float32)")
+
+
+def _ptr(t, name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise DbsaError(EINVAL, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise DbsaError(EINVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise DbsaError(EINVAL, f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device):
+    """Per-device workspace, grown on demand (calls on one stream are ordered)."""
+    import torch
+    if nbytes == 0:
+        return None
+    key = str(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _ws_ptr(ws):
+    return 0 if ws is None else ws.data_ptr()
+
+
+def _ws_size(ws):
+    return 0 if ws is None else ws.numel()
+
+
+def dbsa_workspace_bytes(op, n_q_heads, n_kv_heads, head_dim, dtype, theta=1e4, block_lens=None,
+                         sink=1, j=2, rows=0, batch=1, n_ids=0, max_ctx=0) -> int:
+    lib = load()
+    a = attn_t(n_q_heads, n_kv_heads, head_dim, dtype, theta)
+    b = Blocks(block_lens if block_lens is not None else [1], sink, j)
+    n = lib.dbsa_workspace_bytes(op, ctypes.byref(a), ctypes.byref(b.t), int(rows), int(batch),
+                                 int(n_ids), int(max_ctx))
+    if n == 0:
+        msg = lib.dbsa_last_error().decode()
+        if msg:
+            raise DbsaError(EINVAL, msg)
+    return int(n)
+
+
+def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta: float, scale=None, out=None):
+    """Stage-1 block-sparse prefill of one layer; returns O [N, Hq, d]."""
+    import torch
+    lib = load()
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    b = Blocks(block_lens, sink, j)
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib.dbsa_workspace_bytes(OP_PREFILL, ctypes.byref(a), ctypes.byref(b.t), 0, 1, 0, 0)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q.device)
+    _check(lib.dbsa_prefill(ctypes.byref(a), ctypes.byref(b.t), _ptr(q, "q"),
+                            _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), _ptr(out, "out", q.dtype),
+                            _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    return out
+
+
+def dbsa_append_block(q_new, k_new, v_new, k_cache, v_cache, block_lens, sink: int, j: int,
+                      theta: float, scale=None, out=None):
+    """Encode one new block onto the pool (block_lens = the existing blocks)."""
+    import torch
+    lib = load()
+    new_len, hq, d = q_new.shape
+    hkv = k_new.shape[1]
+    dt = _dtype_code(q_new)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    b = Blocks(block_lens, sink, j)
+    if out is None:
+        out = torch.empty_like(q_new)
+    need = lib.dbsa_workspace_bytes(OP_APPEND, ctypes.byref(a), ctypes.byref(b.t), new_len, 1, 0,
+                                    0)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q_new.device)
+    _check(lib.dbsa_append_block(ctypes.byref(a), ctypes.byref(b.t), int(new_len),
+                                 _ptr(q_new, "q_new"), _ptr(k_new, "k_new", q_new.dtype),
+                                 _ptr(v_new, "v_new", q_new.dtype),
+                                 _ptr(k_cache, "k_cache", q_new.dtype),
+                                 _ptr(v_cache, "v_cache", q_new.dtype), int(k_cache.shape[0]),
+                                 _ptr(out, "out", q_new.dtype), _ws_ptr(ws), _ws_size(ws),
+                                 _stream(q_new.device)))
+    return out
+
+
+def dbsa_gather_rope(k_pool, v_pool, block_lens, ids, theta: float, n_q_heads: Optional[int] = None,
+                     capacity: Optional[int] = None, k_out=None, v_out=None, sink: int = 1,
+                     j: int = 0):
+    """Gather the selected blocks (ids [batch, n_ids], anchor first) and re-rotate K.
+
+    Returns (k_out, v_out, ctx_len) with k_out/v_out [batch, capacity, Hkv, d].
+    """
+    import torch
+    lib = load()
+    _, hkv, d = k_pool.shape
+    dt = _dtype_code(k_pool)
+    a = attn_t(n_q_heads or hkv, hkv, d, dt, theta)
+    b = Blocks(block_lens, sink, j)
+    ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
+    batch, n_ids = ids.shape
+    if capacity is None:
+        lens = np.asarray(block_lens, dtype=np.int64)
+        capacity = int(max(lens[np.clip(r, 0, lens.size - 1)].sum() for r in ids))
+    if k_out is None:
+        k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
+        v_out = torch.empty_like(k_out)
+    ctx = np.zeros(batch, dtype=np.int64)
+    need = lib.dbsa_workspace_bytes(OP_GATHER, ctypes.byref(a), ctypes.byref(b.t), 0, batch, n_ids,
+                                    0)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, k_pool.device)
+    _check(lib.dbsa_gather_rope(ctypes.byref(a), ctypes.byref(b.t),
+                                ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_ids, batch,
+                                _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+                                _ptr(k_out, "k_out", k_pool.dtype),
+                                _ptr(v_out, "v_out", k_pool.dtype), int(k_out.shape[1]),
+                                ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ws_ptr(ws),
+                                _ws_size(ws), _stream(k_pool.device)))
+    return k_out, v_out, ctx
+
+
+def dbsa_query_attn(q, k_new, v_new, k_ctx, v_ctx, ctx_len: Sequence[int], theta: float,
+                    scale=None, out=None):
+    """Query tokens q [batch, n_new, Hq, d] over the gathered cache k_ctx/v_ctx
+    [batch, cap, Hkv, d] holding ctx_len[b] rotated tokens.  Appends the new
+    tokens' K/V to the cache; the caller advances ctx_len by n_new."""
+    import torch
+    lib = load()
+    batch, n_new, hq, d = q.shape
+    hkv = k_new.shape[2]
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    ctx = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int64).reshape(batch))
+    if out is None:
+        out = torch.empty_like(q)
+    if n_new == 0:
+        return out
+    b = Blocks([1], 1, 0)
+    need = lib.dbsa_workspace_bytes(OP_QUERY, ctypes.byref(a), ctypes.byref(b.t), n_new, batch, 0,
+                                    int(ctx.max()) + n_new)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q.device)
+    _check(lib.dbsa_query_attn(ctypes.byref(a), batch, n_new, _ptr(q, "q"),
+                               _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+                               _ptr(k_ctx, "k_ctx", q.dtype), _ptr(v_ctx, "v_ctx", q.dtype),
+                               ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               int(k_ctx.shape[1]), _ptr(out, "out", q.dtype), _ws_ptr(ws),
+                               _ws_size(ws), _stream(q.device)))
+    return out
+
+
+def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k_tail, v_tail,
+                             tail_len: Sequence[int], theta: float, scale=None, out=None):
+    """Query tokens over the selected pool blocks, gathered and re-rotated inside
+    the attention's loads, followed by the row's tail buffer (query/decoded
+    tokens, rotated).  Appends the new tokens to the tail; the caller advances
+    tail_len by n_new."""
+    import torch
+    lib = load()
+    batch, n_new, hq, d = q.shape
+    hkv = k_new.shape[2]
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    b = Blocks(block_lens, 1, 0)
+    ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
+    n_ids = ids.shape[1]
+    tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int64).reshape(batch))
+    if out is None:
+        out = torch.empty_like(q)
+    if n_new == 0:
+        return out
+    lens = np.asarray(block_lens, dtype=np.int64)
+    tp = max(int(lens[np.clip(r, 0, lens.size - 1)].sum()) for r in ids)
+    need = lib.dbsa_workspace_bytes(OP_QUERY_GATHERED, ctypes.byref(a), ctypes.byref(b.t), n_new,
+                                    batch, n_ids, tp + int(tl.max()) + n_new)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q.device)
+    _check(lib.dbsa_query_attn_gathered(
+        ctypes.byref(a), ctypes.byref(b.t), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        n_ids, batch, _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new,
+        _ptr(q, "q"), _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+        _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype),
+        tl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(k_tail.shape[1]),
+        _ptr(out, "out", q.dtype), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    return out

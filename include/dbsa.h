@@ -1,0 +1,189 @@
+/*
+ * dbsa.h - C ABI of the MI355X (gfx950) Dynamic Block-Sparse Attention library.
+ *
+ * The method is the one described on the paper-notes page "Efficient Many-Shot
+ * In-Context Learning with Dynamic Block-Sparse Attention" (zhaoyang97
+ * Paper-Notes, ACL 2025, arXiv 2503.08640), cited below as [Notes, section].
+ *
+ *   Stage 1 [Notes, Method > Stage 1]: the demonstration pool, cut into blocks,
+ *   is encoded once; block i attends to the anchor (sink) block, to the
+ *   previous j blocks and causally to itself, at sequential positions, and K/V
+ *   are cached before the rotary transform.
+ *   Stage 2 [Notes, Method > Stage 2]: per query, the K/V of the retrieved
+ *   blocks (anchor first) are concatenated, RoPE is re-applied at new
+ *   sequential positions, and the query tokens attend to all of it.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are device pointers to contiguous, token-major arrays
+ *    [tokens][heads][head_dim] of the element type `dtype` (bf16 or f32),
+ *    16-byte aligned.  K/V pools are unrotated ("pre-RoPE").
+ *  - Host arrays (block_lens, ids, ctx_len, ...) are read before the call
+ *    returns; the caller may reuse them at once.
+ *  - Positions are token positions.  RoPE is the rotate-half form: pair
+ *    (i, i + d/2) turns by p * theta^(-2i/d).
+ *  - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *  - Every argument is checked on the host before any HIP call.  On any
+ *    non-OK return nothing has been enqueued and dbsa_last_error() describes
+ *    the problem.  DBSA_OK means "enqueued on `stream`" (a hipStream_t, NULL =
+ *    the default stream), not "finished": the caller synchronises.
+ *  - The library allocates no device memory.  Scratch space is the caller's
+ *    workspace `ws` of at least dbsa_workspace_bytes(...) bytes (256-byte
+ *    aligned).  A workspace must not be shared by calls that may overlap.
+ *    Small per-call tables travel host->device through a pinned staging ring
+ *    the library owns (allocated once per device on first use).
+ *  - Calls are thread-safe; error text is thread-local.
+ */
+#ifndef DBSA_H
+#define DBSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  DBSA_OK = 0,
+  DBSA_EINVAL = -1,       /* malformed argument (NULL, range, ids, lengths)     */
+  DBSA_EUNSUPPORTED = -2, /* dtype, head_dim or head counts not supported        */
+  DBSA_ENOSPC = -3,       /* workspace or output capacity too small              */
+  DBSA_EHIP = -4          /* a HIP runtime call failed (text in dbsa_last_error) */
+};
+
+/* Element types. */
+enum { DBSA_BF16 = 0, DBSA_F32 = 1 };
+
+/* Operation selectors for dbsa_workspace_bytes. */
+enum {
+  DBSA_OP_PREFILL = 0,
+  DBSA_OP_APPEND = 1,
+  DBSA_OP_GATHER = 2,
+  DBSA_OP_QUERY = 3,
+  DBSA_OP_QUERY_GATHERED = 4
+};
+
+/* Shape of one attention layer.
+ * n_q_heads % n_kv_heads == 0; head_dim in {64, 128}; dtype DBSA_BF16 or
+ * DBSA_F32; rope_theta > 0; softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct {
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  double rope_theta;
+  float softmax_scale;
+} dbsa_attn_t;
+
+/* The demonstration pool cut into blocks [Notes, Method > Stage 1, item 1].
+ * block_lens: host int32[n_blocks], tokens per block, each >= 1; block 0 is the
+ * anchor b_1.  sink in {0, 1}: whether blocks see the anchor.  j >= 0: number
+ * of previous blocks seen in full (j >= n_blocks - 1 gives full causal
+ * attention).  Total tokens must be < 2^31. */
+typedef struct {
+  const int32_t* block_lens;
+  int32_t n_blocks;
+  int32_t sink;
+  int32_t j;
+} dbsa_blocks_t;
+
+/* Stage 1: block-sparse streaming prefill of one layer
+ * [Notes, Method > Stage 1, items 2-3; Stage 1 implementation note on
+ * skipping masked blocks].
+ *   q: [N][n_q_heads][d], k, v: [N][n_kv_heads][d]  (unrotated; N = sum of
+ *   block_lens).  Row t is rotated at position t, as is key s.
+ *   o: [N][n_q_heads][d] output (the layer's attention output).
+ * k and v are left untouched: they are the pre-RoPE cache. */
+int dbsa_prefill(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                 const void* q, const void* k, const void* v, void* o,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 1, incremental: encode one new block onto an existing pool
+ * [Notes, Method > Stage 1, item 4; Highlights: constant cost per new block].
+ *   existing: the pool's blocks (its N tokens are k_cache/v_cache[0, N)).
+ *   q_new: [new_len][n_q_heads][d]; k_new, v_new: [new_len][n_kv_heads][d].
+ *   k_cache, v_cache: [cache_capacity_tokens][n_kv_heads][d]; the new K/V are
+ *   written unrotated at [N, N + new_len).  o_new: [new_len][n_q_heads][d].
+ * The work (and the workspace) depends on the anchor, the last j blocks and
+ * new_len only, not on N.  DBSA_ENOSPC if N + new_len > cache_capacity_tokens. */
+int dbsa_append_block(const dbsa_attn_t* attn, const dbsa_blocks_t* existing,
+                      int32_t new_len, const void* q_new, const void* k_new,
+                      const void* v_new, void* k_cache, void* v_cache,
+                      int64_t cache_capacity_tokens, void* o_new,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2: gather the selected blocks' cached K/V and re-apply RoPE at the new
+ * sequential positions [Notes, Method > Stage 2, items 1-3; Ablations > dynamic
+ * block ordering: blocks are placed in the order given].
+ *   ids: host int32[batch][n_ids]; row b lists distinct block ids, ids[b][0]
+ *   must be 0 (the anchor is always included).
+ *   k_pool, v_pool: [N][n_kv_heads][d] unrotated pool.
+ *   k_out, v_out: [batch][out_capacity_tokens][n_kv_heads][d]; row b receives
+ *   T'_b = sum of its blocks' lengths tokens: K rotated at 0..T'_b-1, V copied.
+ *   ctx_len_out: host int64[batch] receives T'_b (filled before return).
+ * DBSA_ENOSPC if some T'_b > out_capacity_tokens. */
+int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                     const int32_t* ids, int32_t n_ids, int32_t batch,
+                     const void* k_pool, const void* v_pool, void* k_out, void* v_out,
+                     int64_t out_capacity_tokens, int64_t* ctx_len_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2: query tokens (or one decode step) over a gathered cache
+ * [Notes, Method > Stage 2, item 4].
+ *   q: [batch][n_new][n_q_heads][d]; k_new, v_new: [batch][n_new][n_kv_heads][d]
+ *   (unrotated).  k_ctx, v_ctx: [batch][ctx_capacity][n_kv_heads][d] holding
+ *   ctx_len[b] rotated tokens per row (as written by dbsa_gather_rope or by
+ *   earlier calls).  New token r of row b sits at position ctx_len[b] + r: its
+ *   K (rotated) and V are written to k_ctx/v_ctx there, and it attends to keys
+ *   [0, ctx_len[b] + r].  o: [batch][n_new][n_q_heads][d].
+ *   ctx_len: host int64[batch].  The caller advances it by n_new afterwards.
+ * DBSA_ENOSPC if ctx_len[b] + n_new > ctx_capacity. */
+int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new,
+                    const void* q, const void* k_new, const void* v_new,
+                    void* k_ctx, void* v_ctx, const int64_t* ctx_len,
+                    int64_t ctx_capacity, void* o,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2 with the gather and the re-rotation fused into the attention's K/V
+ * loads [Notes, Method > Stage 2, items 1-4]: nothing is materialised.
+ *   blocks, ids, k_pool, v_pool: as dbsa_gather_rope; the context of row b is
+ *   its T'_b gathered tokens (K rotated on load at 0..T'_b-1) followed by
+ *   tail_len[b] tokens already in k_tail/v_tail ([batch][tail_capacity]
+ *   [n_kv_heads][d], rotated, at positions T'_b + i).
+ *   New token r sits at position T'_b + tail_len[b] + r; its rotated K and V
+ *   are written to k_tail/v_tail at index tail_len[b] + r.
+ *   tail_len: host int64[batch]; the caller advances it by n_new afterwards.
+ *   q, k_new, v_new, o: as dbsa_query_attn.
+ * DBSA_ENOSPC if tail_len[b] + n_new > tail_capacity. */
+int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                             const int32_t* ids, int32_t n_ids, int32_t batch,
+                             const void* k_pool, const void* v_pool, int32_t n_new,
+                             const void* q, const void* k_new, const void* v_new,
+                             void* k_tail, void* v_tail, const int64_t* tail_len,
+                             int64_t tail_capacity, void* o,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the operation needs.
+ *   op: DBSA_OP_*.  blocks: the pool (for DBSA_OP_APPEND, the existing pool).
+ *   rows: PREFILL ignores it; APPEND: new_len; QUERY / QUERY_GATHERED: n_new;
+ *   GATHER: ignored.  batch: Stage-2 batch (ignored for Stage 1).
+ *   n_ids: ids per row (GATHER, QUERY_GATHERED), else ignored.
+ *   max_ctx: QUERY: the largest ctx_len[b] + n_new the call will see;
+ *   QUERY_GATHERED: the largest T'_b + tail_len[b] + n_new; else ignored.
+ * Returns 0 and sets the error text on invalid arguments. */
+size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                            int64_t rows, int32_t batch, int32_t n_ids, int64_t max_ctx);
+
+/* Text of the last non-OK return on this thread ("" if none). */
+const char* dbsa_last_error(void);
+
+/* Library version string. */
+const char* dbsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBSA_H */
