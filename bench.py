@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the DBSA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic batch of the
+Llama-2-7B-shaped layer (30 blocks x 1024 tokens, 32 MHA heads, d = 128,
+bf16, sink + previous 2 blocks):
+  * dbsa_prefill            block-sparse streaming prefill of the pool
+                            (mask -> key-tile walk, RoPE, flash attention;
+                            the unrotated K/V stay as the cache),
+  * dbsa_gather_rope        gather of anchor + 9 selected blocks, re-RoPE,
+  * dbsa_query_attn         64 query tokens over the gathered cache.
+Prints one JSON line.  `value` = prefill FLOP on executed (unmasked) 64-key
+tiles per step / step time.  The roofline object is for the dominant call,
+dbsa_prefill (K-tile pack + flash kernel), timed with HIP events on the
+stream it runs on.  The CPU baseline is the fp64 oracle on a bounded row
+sample of the same workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KEY_TILE, ROW_TILE = 64, 256
+PREFILL_PROFILE = os.path.join(ROOT, "profiles", "k_prefill_bf16_llama2_30x1024.md")
+
+
+def visible_pairs(lens, sink, j):
+    """Sum over rows of the visible-key count (interval form of the block mask)."""
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total = 0
+    for i, L in enumerate(lens):
+        lo = max(i - j, 0)
+        extra = lens[0] if (sink and lo > 0) else 0
+        total += int(L) * int(off[i] - off[lo] + extra) + int(L) * (int(L) + 1) // 2
+    return total
+
+
+def executed_tiles(lens, sink, j):
+    """64-key tiles the prefill walks, summed over 128-row query tiles."""
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    nb = len(lens)
+    blk_of = lambda t: int(np.searchsorted(off, t, side="right") - 1)
+    lo_of = lambda t: int(off[max(min(blk_of(t), nb - 1) - j, 0)])
+    tiles = 0
+    for r0 in range(0, n, ROW_TILE):
+        r1 = min(r0 + ROW_TILE, n)
+        w0 = lo_of(r0) // KEY_TILE
+        w1 = -(-r1 // KEY_TILE)
+        ns = min(-(-int(off[1]) // KEY_TILE), w0) if (sink and lo_of(r1 - 1) > 0) else 0
+        tiles += ns + (w1 - w0)
+    return tiles
+
+
+def profile_traffic(path, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t:
+        return None
+    cur = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    return float(t.group(1)) if m.group(1) == cur else None
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate oracle time budget for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-op", choices=["prefill", "gather", "query", "fused", "copy"],
+                    help="run only this operation --steps times (for rocprofv3); prints timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the DBSA hot path here runs on a single "
+              "MI355X (no multi-GPU path is built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_sink_amd import dbsa
+    from block_sparse_attention_sink_amd.inputs import randn, workload
+
+    dbsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workload(2)
+    lens, sink, j, theta = w.block_lens, w.sink, w.j, w.theta
+    n, hq, hkv, d = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
+    ids = w.ids
+    n_new = w.n_new
+    tp = int(lens[ids[0]].sum())
+
+    q = randn((n, hq, d), 1001, "bf16", dev)
+    k = randn((n, hkv, d), 1002, "bf16", dev)
+    v = randn((n, hkv, d), 1003, "bf16", dev)
+    o = torch.empty_like(q)
+    qn = randn((1, n_new, hq, d), 1004, "bf16", dev)
+    kn = randn((1, n_new, hkv, d), 1005, "bf16", dev)
+    vn = randn((1, n_new, hkv, d), 1006, "bf16", dev)
+    on = torch.empty_like(qn)
+    kg = torch.empty((1, tp + n_new, hkv, d), dtype=torch.bfloat16, device=dev)
+    vg = torch.empty_like(kg)
+    ctx = np.array([tp], np.int64)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+
+    def step(record=False):
+        e = [ev() for _ in range(4)] if record else None
+        if record:
+            e[0].record()
+        dbsa.dbsa_prefill(q, k, v, lens, sink, j, theta, out=o)
+        if record:
+            e[1].record()
+        dbsa.dbsa_gather_rope(k, v, lens, ids, theta, k_out=kg, v_out=vg)
+        if record:
+            e[2].record()
+        dbsa.dbsa_query_attn(qn, kn, vn, kg, vg, ctx, theta, out=on)
+        if record:
+            e[3].record()
+            marks.append(e)
+
+    if args.profile_op:
+        tail_k = torch.empty((1, n_new, hkv, d), dtype=torch.bfloat16, device=dev)
+        tail_v = torch.empty_like(tail_k)
+        copy_src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        copy_dst = torch.empty_like(copy_src)
+        ops = {
+            "prefill": lambda: dbsa.dbsa_prefill(q, k, v, lens, sink, j, theta, out=o),
+            "gather": lambda: dbsa.dbsa_gather_rope(k, v, lens, ids, theta, k_out=kg, v_out=vg),
+            "query": lambda: dbsa.dbsa_query_attn(qn, kn, vn, kg, vg, ctx, theta, out=on),
+            "fused": lambda: dbsa.dbsa_query_attn_gathered(qn, kn, vn, k, v, lens, ids, tail_k,
+                                                           tail_v, [0], theta, out=on),
+            "copy": lambda: copy_dst.copy_(copy_src),
+        }
+        fn = ops[args.profile_op]
+        dbsa.dbsa_gather_rope(k, v, lens, ids, theta, k_out=kg, v_out=vg)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a0, a1 = ev(), ev()
+        a0.record()
+        for _ in range(args.steps):
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_op": args.profile_op, "steps": args.steps,
+                          "ms_per_call": a0.elapsed_time(a1) / args.steps,
+                          "copy_bytes_read": copy_src.numel() * 4}))
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = ev(), ev()
+    t0.record()
+    for _ in range(args.steps):
+        step(record=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_prefill = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    ms_gather = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    ms_query = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+
+    pairs = visible_pairs(lens, sink, j)
+    exact_flop = 4.0 * d * hq * pairs
+    tiles = executed_tiles(lens, sink, j)
+    tile_flop = 4.0 * d * hq * tiles * ROW_TILE * KEY_TILE
+    value = tile_flop / (ms_step * 1e-3) / 1e12
+    achieved = exact_flop / (ms_prefill * 1e-3) / 1e12
+
+    # Stage 2 alone, last-level cache flushed between repetitions (1 GiB write).
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    kv_bytes = tp * hkv * d * 2 * 2
+    io_bytes = (qn.numel() + kn.numel() + vn.numel() + on.numel()) * 2
+    tail_k = torch.empty((1, n_new, hkv, d), dtype=torch.bfloat16, device=dev)
+    tail_v = torch.empty_like(tail_k)
+
+    def timed(fn, reps=10):
+        ts = []
+        for _ in range(reps + 2):
+            flush.zero_()
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts[2:]))
+
+    g_ms = timed(lambda: dbsa.dbsa_gather_rope(k, v, lens, ids, theta, k_out=kg, v_out=vg))
+    q_ms = timed(lambda: dbsa.dbsa_query_attn(qn, kn, vn, kg, vg, ctx, theta, out=on))
+    f_ms = timed(lambda: dbsa.dbsa_query_attn_gathered(qn, kn, vn, k, v, lens, ids, tail_k, tail_v,
+                                                       [0], theta, out=on))
+    stage2 = {
+        "context_tokens": tp, "query_tokens": n_new,
+        "gather_rope": {"us": g_ms * 1e3, "GB/s": 2 * kv_bytes / (g_ms * 1e-3) / 1e9,
+                        "bytes": 2 * kv_bytes},
+        "query_attn": {"us": q_ms * 1e3, "GB/s": (kv_bytes + io_bytes) / (q_ms * 1e-3) / 1e9,
+                       "bytes": kv_bytes + io_bytes},
+        "gather_plus_query": {"us": (g_ms + q_ms) * 1e3,
+                              "GB/s": (kv_bytes + io_bytes) / ((g_ms + q_ms) * 1e-3) / 1e9},
+        "fused_gather_query": {"us": f_ms * 1e3,
+                               "GB/s": (kv_bytes + io_bytes) / (f_ms * 1e-3) / 1e9,
+                               "frac_hbm": (kv_bytes + io_bytes) / (f_ms * 1e-3) / 1e9
+                               / PEAK_HBM_GBS},
+        "note": "algorithmic bytes = unrotated K+V of the gathered tokens read once + Q, new K/V, "
+                "O; gather counts its read and write; cache flushed between repetitions",
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import dbsa_oracle as orc
+        h = lambda t: t.float().cpu().numpy().astype(np.float64)
+        qh, kh, vh = h(q), h(k), h(v)
+        rng = np.random.default_rng(7)
+        # Rows from every block, sized so the oracle runs about --cpu-seconds.
+        probe = np.sort(rng.choice(n, 32, replace=False))
+        t = time.perf_counter()
+        orc.prefill(qh, kh, vh, lens, sink, j, theta, rows=probe)
+        per_row = (time.perf_counter() - t) / probe.size
+        n_rows = int(np.clip(args.cpu_seconds / max(per_row, 1e-6), 32, 4096))
+        rows = np.sort(rng.choice(n, n_rows, replace=False))
+        t = time.perf_counter()
+        orc.prefill(qh, kh, vh, lens, sink, j, theta, rows=rows)
+        secs = time.perf_counter() - t
+        off = np.concatenate([[0], np.cumsum(lens)])
+        blk = np.searchsorted(off, rows, side="right") - 1
+        lo = off[np.maximum(blk - j, 0)]
+        vis = (rows - lo + 1) + np.where((lo > 0) & bool(sink), lens[0], 0)
+        cpu = {"value": 4.0 * d * hq * float(vis.sum()) / secs / 1e12, "unit": "TFLOP/s",
+               "cores": cpu_threads(), "kind": "oracle",
+               "sample": f"dbsa_prefill oracle (fp64 masked-dense NumPy) on {n_rows} random rows "
+                         f"x all {hq} heads of the same workload, {secs:.1f} s; value counts the "
+                         "exact visible pairs of the sampled rows"}
+
+    traffic = profile_traffic(PREFILL_PROFILE, os.path.join(
+        ROOT, "block_sparse_attention_sink_amd", "csrc", "k_stage1.hip"))
+    out = {
+        "metric": "DBSA prefill TFLOP/s (unmasked tiles) + gather/query-attn GB/s, % roofline",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V (seeded), no model weights",
+        "config": {"workload": w.name, "n_tokens": n, "n_blocks": int(lens.size),
+                   "block_len": int(lens[0]), "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+                   "sink": sink, "j": j, "rope_theta": theta, "stage2_blocks": int(ids.shape[1]),
+                   "stage2_context": tp, "query_tokens": n_new, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "dbsa_prefill call = k_pack_bf16 + k_prefill_bf16",
+                     "ms_per_launch": ms_prefill,
+                     "algorithmic_flop_per_launch": exact_flop},
+        "prefill": {"exact_pairs_per_head": pairs, "exact_TFLOP": exact_flop / 1e12,
+                    "executed_tiles_128x64_per_head": tiles,
+                    "executed_tile_TFLOP": tile_flop / 1e12,
+                    "exact_TFLOP/s": exact_flop / (ms_prefill * 1e-3) / 1e12,
+                    "executed_tile_TFLOP/s": tile_flop / (ms_prefill * 1e-3) / 1e12},
+        "step_breakdown_ms": {"prefill": ms_prefill, "gather_rope": ms_gather,
+                              "query_attn": ms_query},
+        "stage2": stage2,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
 ]
+# Kernel files only: scores and probabilities are never NaN (masked scores are
+# -inf, which stays honoured), so max/min need no NaN canonicalisation.  The
+# host file keeps full IEEE semantics for its argument checks.
+KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans"], "k_stage2.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -38,7 +42,8 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *FLAGS, *KERNEL_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         for cmd, err in zip(cmds, ex.map(_run, cmds)):
             if verbose and err.strip():

@@ -14,8 +14,9 @@ namespace dbsa {
 // ---------------------------------------------------------------------------
 constexpr int kKeyTile = 64;      // keys per K/V tile (one LDS stage)
 constexpr int kRowsPerWave = 32;  // query rows per wavefront (MFMA N dimension)
-constexpr int kPrefillWaves = 4;  // waves per prefill workgroup
-constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 128 query rows per workgroup
+constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
+constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
+constexpr int kPrefillStages = 4;  // LDS ring of K/V tiles (3 tiles of lookahead)
 constexpr int kQueryMaxWaves = 8;  // waves per Stage-2 workgroup (<= 256 packed rows)
 constexpr int kMaxHalf = 64;       // head_dim / 2 upper bound (head_dim <= 128)
 

@@ -19,7 +19,7 @@
 namespace dbsa {
 
 // ---------------------------------------------------------------------------
-// K rotation + V transpose into tile images.
+// K rotation + V transpose into tile images (the LDS byte images, see TileGeom).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
@@ -46,8 +46,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
   }
   const int64_t tile = (int64_t)g * a.n_slots + slot;
   u32x4* ko = reinterpret_cast<u32x4*>(a.k_tiles) + tile * (64 * CR);
-  ko[key * CR + k_chunk_phys<D>(key, c)] = k1;
-  ko[key * CR + k_chunk_phys<D>(key, c + CP)] = k2;
+  using Gm = TileGeom<D>;
+  ko[key * CR + Gm::k_phys(key, c)] = k1;
+  ko[key * CR + Gm::k_phys(key, c + CP)] = k2;
 
   *reinterpret_cast<u32x4*>(&vs[key][8 * c]) = v1;
   *reinterpret_cast<u32x4*>(&vs[key][D / 2 + 8 * c]) = v2;
@@ -65,25 +66,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
       const uint32_t hi = vs[kbase + vt_key_of_pos(p + 1)][drow];
       w[r >> 1] = lo | (hi << 16);
     }
-    vo[drow * 8 + vt_chunk_phys(drow, ch)] = u32x4{w[0], w[1], w[2], w[3]};
+    vo[drow * 8 + Gm::v_phys(drow, ch)] = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
 // ---------------------------------------------------------------------------
 // Block-sparse flash prefill, bf16 in / bf16 out, fp32 accumulation.
 //
-// Workgroup = 4 wavefronts = 128 query rows of one query head; wave w owns
-// rows r0 + 32w .. +31, lane l holds row (l % 32) and, in its half h = l / 32,
-// half of every 64-key tile's scores for that row.
+// Workgroup = 8 wavefronts = 256 query rows of one query head; wave w owns
+// rows r0 + 32w .. +31 (lane layout: see Flash).  The workgroup walks the
+// 64-key tiles that meet its rows' visible intervals through a ring of 4 LDS
+// stages filled by direct global->LDS loads, 3 tiles ahead of the compute.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_prefill_bf16(PrefillArgs a) {
-  constexpr int KS = D / 16;          // MFMA k-steps over the head dim
-  constexpr int OT = D / 32;          // 32-row O^T tiles
-  constexpr int CR = D / 8;           // 16-byte chunks per K row
-  constexpr int TU4 = 64 * D / 8;     // u32x4 per tile matrix
-  constexpr int PER_T = TU4 / 256;    // u32x4 per thread per matrix
-  __shared__ u32x4 lds[2][2][TU4];    // [stage][K, V^T]
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillArgs a) {
+  using Gm = TileGeom<D>;
+  constexpr int KS = D / 16;
+  constexpr int NST = kPrefillStages;
+  constexpr int LPW = 2 * Gm::TU4 / 64 / kPrefillWaves;  // loads per wave per tile
+  __shared__ __align__(16) char lds[NST * Gm::STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
@@ -131,129 +132,54 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(PrefillArgs a) {
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
 
-  f32x16 oacc[OT];
-#pragma unroll
-  for (int m = 0; m < OT; ++m) oacc[m] = f32x16{};
-  float m_run = kMaxFloor, l_run = 0.0f;
+  Flash<D> fl;
+  fl.init();
 
-  const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * TU4;
-  const u32x4* vbase = reinterpret_cast<const u32x4*>(a.v_tiles) + (int64_t)g * a.n_slots * TU4;
+  const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
+  const u32x4* vbase = reinterpret_cast<const u32x4*>(a.v_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
   auto tile_of = [&](int it) { return it < nsink ? it : win0 + (it - nsink); };
   auto slot_of = [&](int kt) {
     return kt < a.sink_tiles ? kt : a.sink_tiles + (kt - a.win_tile0);
   };
+  // Stage tile `it` into LDS stage `buf` (K image then V^T image), no registers.
+  auto load = [&](int it, int buf) {
+    const int64_t sl = (int64_t)slot_of(tile_of(it)) * Gm::TU4;
+    char* st = lds + buf * Gm::STAGE;
+    copy_to_lds(kbase + sl, st, Gm::TU4, wave, kPrefillWaves, lane);
+    copy_to_lds(vbase + sl, st + Gm::KBYTES, Gm::TU4, wave, kPrefillWaves, lane);
+  };
+  int koff[KS], voff[4];
+  lane_offsets<D>(col, hh, koff, voff);
 
-  u32x4 kreg[PER_T], vreg[PER_T];
-  {
-    const int64_t s0 = (int64_t)slot_of(tile_of(0)) * TU4;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      lds[0][0][tid + 256 * i] = kbase[s0 + tid + 256 * i];
-      lds[0][1][tid + 256 * i] = vbase[s0 + tid + 256 * i];
-    }
-  }
-  __syncthreads();
-
+  // Ring of NST stages: tile it+NST-1 is requested while tile it is computed.
+  for (int p = 0; p < NST - 1 && p < n_tiles; ++p) load(p, p);
   for (int it = 0; it < n_tiles; ++it) {
-    const int cur = it & 1;
-    const int kt = tile_of(it);
-    if (it + 1 < n_tiles) {
-      const int64_t sn = (int64_t)slot_of(tile_of(it + 1)) * TU4;
-#pragma unroll
-      for (int i = 0; i < PER_T; ++i) {
-        kreg[i] = kbase[sn + tid + 256 * i];
-        vreg[i] = vbase[sn + tid + 256 * i];
-      }
-    }
-    const u32x4* Kl = lds[cur][0];
-    const u32x4* Vl = lds[cur][1];
-
-    // S^T (keys x rows) for the two 32-key halves of the tile.
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka0 =
-          __builtin_bit_cast(bf16x8, Kl[col * CR + k_chunk_phys<D>(col, 2 * ks + hh)]);
-      const bf16x8 ka1 = __builtin_bit_cast(
-          bf16x8, Kl[(32 + col) * CR + k_chunk_phys<D>(32 + col, 2 * ks + hh)]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
-    }
-
+    // Tile `it` has landed once at most the loads of the tiles after it
+    // (issued earlier) are still outstanding; the barrier then also certifies
+    // that every wave is done with the stage refilled below.
+    wait_vm(LPW * min(NST - 2, n_tiles - 1 - it));
+    barrier_nofence();
+    if (it + NST - 1 < n_tiles) load(it + NST - 1, (it + NST - 1) % NST);
+    const int k0 = tile_of(it) * kKeyTile;
     // Element mask only on tiles some row cannot fully see.
-    const int k0 = kt * kKeyTile;
     const bool full = (k0 + kKeyTile - 1 <= r0) &&
                       (k0 >= lo_last || (a.sink && k0 + kKeyTile <= sink_end));
-    if (!full) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kr = (i >> 2) * 8 + hh * 4 + (i & 3);
-        const int sa = k0 + kr, sb = k0 + 32 + kr;
-        const bool va = sa <= t && (sa >= lo_t || sa < sink_end);
-        const bool vb = sb <= t && (sb >= lo_t || sb < sink_end);
-        s0[i] = va ? s0[i] : kNegInf;
-        s1[i] = vb ? s1[i] : kNegInf;
-      }
-    }
-
-    // Online softmax (base 2; scores already carry scale * log2 e).
-    float mx = kMaxFloor;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = __builtin_amdgcn_exp2f(s0[i] - m_new);
-      s1[i] = __builtin_amdgcn_exp2f(s1[i] - m_new);
-      rs += s0[i] + s1[i];
-    }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int m = 0; m < OT; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
-
-    // P^T as the B operand: k-step kk covers keys 16kk .. 16kk+15.
-    bf16x8 pb[4];
-    pb[0] = pack_p<0>(s0);
-    pb[1] = pack_p<8>(s0);
-    pb[2] = pack_p<0>(s1);
-    pb[3] = pack_p<8>(s1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int m = 0; m < OT; ++m) {
-        const int drow = m * 32 + col;
-        const bf16x8 va =
-            __builtin_bit_cast(bf16x8, Vl[drow * 8 + vt_chunk_phys(drow, 2 * kk + hh)]);
-        oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], oacc[m], 0, 0, 0);
-      }
-
-    if (it + 1 < n_tiles) {
-#pragma unroll
-      for (int i = 0; i < PER_T; ++i) {
-        lds[cur ^ 1][0][tid + 256 * i] = kreg[i];
-        lds[cur ^ 1][1][tid + 256 * i] = vreg[i];
-      }
-    }
-    __syncthreads();
+    const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
+    fl.tile(lds + (it % NST) * Gm::STAGE, koff, voff, qb, !full,
+            [=](int kr) { return kr <= tt && (kr >= lt || kr < se); });
   }
 
-  l_run += __shfl_xor(l_run, 32);
+  const float lsum = fl.total();
   if (t < r1) {
-    const float inv = 1.0f / l_run;
+    const float inv = 1.0f / lsum;
     uint16_t* op = static_cast<uint16_t*>(a.o) + ((int64_t)(t - a.q_row0) * a.hq + head) * D;
 #pragma unroll
-    for (int m = 0; m < OT; ++m)
+    for (int m = 0; m < D / 32; ++m)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = m * 32 + q4 * 8 + hh * 4;
-        const u32x2 w = {pack_bf16x2(oacc[m][4 * q4 + 0] * inv, oacc[m][4 * q4 + 1] * inv),
-                         pack_bf16x2(oacc[m][4 * q4 + 2] * inv, oacc[m][4 * q4 + 3] * inv)};
+        const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
+                         pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + d) = w;
       }
   }
@@ -360,9 +286,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStre
   }
   const dim3 grid(a.n_qtiles * a.hq);
   if (head_dim == 128)
-    hipLaunchKernelGGL(k_prefill_bf16<128>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_prefill_bf16<128>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_prefill_bf16<64>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_prefill_bf16<64>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -140,11 +140,11 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // ---------------------------------------------------------------------------
 template <int D, bool FUSED>
 __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
-  constexpr int KS = D / 16, OT = D / 32, CR = D / 8, CP = D / 16;
-  constexpr int TU4 = 64 * D / 8;
+  using Gm = TileGeom<D>;
+  constexpr int KS = D / 16, CP = D / 16;
   constexpr int UNITS = 64 * CP;         // (key, chunk pair) units per tile
   constexpr int UPT = (UNITS + 511) / 512;
-  __shared__ u32x4 lds[2][2][TU4];
+  __shared__ __align__(16) char lds[2 * Gm::STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
   const uint16_t* kctx = static_cast<const uint16_t*>(a.k_ctx);
   const uint16_t* vctx = static_cast<const uint16_t*>(a.v_ctx);
 
-  // Staging registers of one tile: this thread's units.
+  // Staging registers of one tile: this thread's (key, chunk pair) units.
   u32x4 k1[UPT], k2[UPT], v1[UPT], v2[UPT];
   int upos[UPT];
   bool urot[UPT];
@@ -226,37 +226,38 @@ __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
       }
     }
   };
+  // Rotate (pool tokens), then write K rows and V^T columns into a stage.
   auto stage = [&](int buf) {
-    u32x4* Kl = lds[buf][0];
-    uint16_t* Vh = reinterpret_cast<uint16_t*>(lds[buf][1]);
+    char* st = lds + buf * Gm::STAGE;
 #pragma unroll
     for (int x = 0; x < UPT; ++x) {
       const int unit = tid + 512 * x;
       if (unit >= UNITS) continue;
       const int key = unit / CP, c = unit - key * CP;
       if (FUSED && urot[x]) rope_rotate_chunk(k1[x], k2[x], upos[x], a.freq, 8 * c);
-      Kl[key * CR + k_chunk_phys<D>(key, c)] = k1[x];
-      Kl[key * CR + k_chunk_phys<D>(key, c + CP)] = k2[x];
-      // V^T: element d of this key goes to row d, position pos_of_key within its group.
+      *reinterpret_cast<u32x4*>(st + key * Gm::KROW + Gm::k_phys(key, c) * 16) = k1[x];
+      *reinterpret_cast<u32x4*>(st + key * Gm::KROW + Gm::k_phys(key, c + CP) * 16) = k2[x];
+      // V^T: head dim d of this key goes to row d, chunk ch, element e.
       const int p = vt_pos_of_key(key & 15);
       const int ch = 2 * (key >> 4) + (p >> 3), e = p & 7;
+      char* vt = st + Gm::KBYTES + e * 2;
       const uint32_t w1[4] = {v1[x].x, v1[x].y, v1[x].z, v1[x].w};
       const uint32_t w2[4] = {v2[x].x, v2[x].y, v2[x].z, v2[x].w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int d1 = 8 * c + q, d2 = D / 2 + 8 * c + q;
-        const uint16_t e1 = (uint16_t)(q & 1 ? w1[q >> 1] >> 16 : w1[q >> 1]);
-        const uint16_t e2 = (uint16_t)(q & 1 ? w2[q >> 1] >> 16 : w2[q >> 1]);
-        Vh[(d1 * 8 + vt_chunk_phys(d1, ch)) * 8 + e] = e1;
-        Vh[(d2 * 8 + vt_chunk_phys(d2, ch)) * 8 + e] = e2;
+        *reinterpret_cast<uint16_t*>(vt + d1 * Gm::VROW + Gm::v_phys(d1, ch) * 16) =
+            (uint16_t)(q & 1 ? w1[q >> 1] >> 16 : w1[q >> 1]);
+        *reinterpret_cast<uint16_t*>(vt + d2 * Gm::VROW + Gm::v_phys(d2, ch) * 16) =
+            (uint16_t)(q & 1 ? w2[q >> 1] >> 16 : w2[q >> 1]);
       }
     }
   };
 
-  f32x16 oacc[OT];
-#pragma unroll
-  for (int m = 0; m < OT; ++m) oacc[m] = f32x16{};
-  float m_run = kMaxFloor, l_run = 0.0f;
+  Flash<D> fl;
+  fl.init();
+  int koff[KS], voff[4];
+  lane_offsets<D>(col, hh, koff, voff);
 
   if (it0 < it1) {
     fetch(it0);
@@ -267,94 +268,44 @@ __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
     const int cur = (it - it0) & 1;
     if (it + 1 < it1) fetch(it + 1);
     if (wave_live) {
-      const u32x4* Kl = lds[cur][0];
-      const u32x4* Vl = lds[cur][1];
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka0 =
-            __builtin_bit_cast(bf16x8, Kl[col * CR + k_chunk_phys<D>(col, 2 * ks + hh)]);
-        const bf16x8 ka1 = __builtin_bit_cast(
-            bf16x8, Kl[(32 + col) * CR + k_chunk_phys<D>(32 + col, 2 * ks + hh)]);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
-      }
+      const char* st = lds + cur * Gm::STAGE;
       const int u0 = it * kKeyTile;
-      if (u0 + kKeyTile - 1 > pos0) {  // some key after the first new token: causal mask
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = (i >> 2) * 8 + hh * 4 + (i & 3);
-          s0[i] = (u0 + kr <= qpos) ? s0[i] : kNegInf;
-          s1[i] = (u0 + 32 + kr <= qpos) ? s1[i] : kNegInf;
-        }
-      }
-      float mx = kMaxFloor;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float rs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = __builtin_amdgcn_exp2f(s0[i] - m_new);
-        s1[i] = __builtin_amdgcn_exp2f(s1[i] - m_new);
-        rs += s0[i] + s1[i];
-      }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int m = 0; m < OT; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
-      bf16x8 pb[4];
-      pb[0] = pack_p<0>(s0);
-      pb[1] = pack_p<8>(s0);
-      pb[2] = pack_p<0>(s1);
-      pb[3] = pack_p<8>(s1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int m = 0; m < OT; ++m) {
-          const int drow = m * 32 + col;
-          const bf16x8 va =
-              __builtin_bit_cast(bf16x8, Vl[drow * 8 + vt_chunk_phys(drow, 2 * kk + hh)]);
-          oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], oacc[m], 0, 0, 0);
-        }
+      const int lim = qpos - u0;  // keys kr <= lim are visible (causal over new tokens)
+      fl.tile(st, koff, voff, qb, u0 + kKeyTile - 1 > pos0, [=](int kr) { return kr <= lim; });
     }
     if (it + 1 < it1) stage(cur ^ 1);
     __syncthreads();
   }
 
   if (!live) return;
-  l_run += __shfl_xor(l_run, 32);
+  const float lsum = fl.total();
   if (a.n_split == 1) {
-    const float inv = 1.0f / l_run;
+    const float inv = 1.0f / lsum;
     uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
 #pragma unroll
-    for (int m = 0; m < OT; ++m)
+    for (int m = 0; m < D / 32; ++m)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = m * 32 + q4 * 8 + hh * 4;
-        const u32x2 w = {pack_bf16x2(oacc[m][4 * q4 + 0] * inv, oacc[m][4 * q4 + 1] * inv),
-                         pack_bf16x2(oacc[m][4 * q4 + 2] * inv, oacc[m][4 * q4 + 3] * inv)};
+        const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
+                         pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + d) = w;
       }
   } else {
     const int64_t prow = (((int64_t)b * a.hkv + g) * a.n_split + split) * a.rows + rho;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int m = 0; m < OT; ++m)
+    for (int m = 0; m < D / 32; ++m)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = m * 32 + q4 * 8 + hh * 4;
         *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{oacc[m][4 * q4 + 0], oacc[m][4 * q4 + 1], oacc[m][4 * q4 + 2],
-                  oacc[m][4 * q4 + 3]};
+            f32x4{fl.o[m][4 * q4 + 0], fl.o[m][4 * q4 + 1], fl.o[m][4 * q4 + 2],
+                  fl.o[m][4 * q4 + 3]};
       }
     if (hh == 0) {
-      a.part_ml[prow * 2 + 0] = m_run;
-      a.part_ml[prow * 2 + 1] = l_run;
+      a.part_ml[prow * 2 + 0] = fl.m;
+      a.part_ml[prow * 2 + 1] = lsum;
     }
   }
 }
@@ -368,11 +319,17 @@ __global__ __launch_bounds__(D) void k_combine(CombineArgs a) {
   const int G = a.hq / a.hkv;
   const int r = rho / G, head = g * G + rho % G;
   const int64_t base = ((int64_t)b * a.hkv + g) * a.n_split;
-  float M = kMaxFloor;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.rows + rho) * 2]);
+  // Reference = largest split reference among splits that saw a key; splits
+  // with no keys (l = 0) contribute nothing.
+  float M = kNegInf;
+  for (int s = 0; s < a.n_split; ++s) {
+    const int64_t prow = (base + s) * a.rows + rho;
+    if (a.part_ml[prow * 2 + 1] > 0.0f) M = fmaxf(M, a.part_ml[prow * 2]);
+  }
   float L = 0.0f, acc = 0.0f;
   for (int s = 0; s < a.n_split; ++s) {
     const int64_t prow = (base + s) * a.rows + rho;
+    if (!(a.part_ml[prow * 2 + 1] > 0.0f)) continue;
     const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
     L += w * a.part_ml[prow * 2 + 1];
     acc += w * a.part_o[prow * D + d];
