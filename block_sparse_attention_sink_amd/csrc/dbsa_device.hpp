@@ -89,6 +89,15 @@ __device__ __forceinline__ void rotate_chunk(u32x4& x1, u32x4& x2, const float (
   x2 = u32x4{ob[0], ob[1], ob[2], ob[3]};
 }
 
+// Rotation of one chunk pair at `pos` with the 8 frequencies held in registers.
+__device__ __forceinline__ void rope_rotate_chunk_f(u32x4& x1, u32x4& x2, int64_t pos,
+                                                    const double (&fr)[8]) {
+  float c[8], s[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) rope_cs(pos, fr[r], c[r], s[r]);
+  rotate_chunk(x1, x2, c, s);
+}
+
 // Rotation of one chunk pair at `pos` for frequencies i0 .. i0+7.
 __device__ __forceinline__ void rope_rotate_chunk(u32x4& x1, u32x4& x2, int64_t pos,
                                                   const RopeFreq& f, int i0,
@@ -100,40 +109,38 @@ __device__ __forceinline__ void rope_rotate_chunk(u32x4& x1, u32x4& x2, int64_t 
 
 
 // ---------------------------------------------------------------------------
-// Tile layouts (one 64-key tile of one KV head).
-//
-//   K tile   [64 keys][D] bf16, rotated                 (KBYTES)
-//   V^T tile [D][64 keys] bf16; inside each 16-key group the keys are stored
-//            in the order the MFMA result layout hands out P (vt_key_of_pos),
-//            so one 16-byte read gives a lane the 8 keys it contracts over.
+// Tile layouts (one 64-key tile of one KV head), both [64 keys][D] bf16:
+//   K tile  rotated keys; read as the A operand of S^T = K Q^T (16 bytes/lane).
+//   V tile  values in their natural layout; read with ds_read_b64_tr_b16 so
+//           each lane receives 4 keys of one head dim (the A operand of
+//           O^T = V^T P^T) without any transpose pass.
 // Rows are split in 16-byte chunks and chunk c of row r is stored at chunk
-// c ^ swz(r): 16 lanes reading the same logical chunk of 16 consecutive rows
-// then hit 16 distinct bank groups.  The global tile images written by the
-// pack step are byte-for-byte the LDS images, so staging is a linear copy.
+// c ^ swz(r), chosen so the lanes of one read hit distinct bank groups.  K
+// tiles of the prefill are written by the pack step as exactly this LDS image;
+// V tiles (and Stage-2 K tiles) are staged straight from the token-major
+// tensors with per-lane source addresses that realise the same placement.
 // ---------------------------------------------------------------------------
 template <int D>
 struct TileGeom {
-  static constexpr int KROW = D * 2;                // K row bytes
-  static constexpr int VROW = kKeyTile * 2;         // V^T row bytes (128)
-  static constexpr int KBYTES = kKeyTile * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;     // one LDS stage (K + V^T)
+  static constexpr int ROW = D * 2;                 // row bytes (K and V)
+  static constexpr int KBYTES = kKeyTile * ROW;
+  static constexpr int VBYTES = kKeyTile * ROW;
+  static constexpr int STAGE = KBYTES + VBYTES;     // one LDS stage (K + V)
   static constexpr int TU4 = kKeyTile * D / 8;      // 16-byte chunks per tile matrix
-  static constexpr int KCR = D / 8;                 // chunks per K row
+  static constexpr int KCR = D / 8;                 // chunks per row
+  static constexpr int KROW = ROW;
+  // K rows: 16 lanes read one logical chunk of 16 consecutive rows.
   static __device__ __forceinline__ int k_phys(int row, int c) {
     if constexpr (D == 128) return c ^ (row & 15);
     else return c ^ ((row >> 1) & 7);
   }
-  static __device__ __forceinline__ int v_phys(int row, int c) { return c ^ ((row >> 1) & 7); }
+  // V rows: a 16-lane transposed read covers 4 consecutive rows x 32 bytes;
+  // the 4 rows land in 4 different 64-byte groups.
+  static __device__ __forceinline__ int v_phys(int row, int c) {
+    if constexpr (D == 128) return c ^ (4 * (row & 3));
+    else return c ^ (4 * (row & 1));
+  }
 };
-
-// Key (0..15, within its 16-key group) stored at position p (0..15), and back.
-__device__ __forceinline__ int vt_key_of_pos(int p) {
-  return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
-}
-__device__ __forceinline__ int vt_pos_of_key(int k) {
-  return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
-}
 
 // Eight probabilities of one MFMA result (registers B .. B+7) as a bf16 B operand.
 template <int B>
@@ -285,73 +292,246 @@ struct Flash {
     l += ra + rb;
   }
 
-  // O^T += V^T P^T (V^T fragments from LDS); k-step outer, OT independent chains.
-  __device__ __forceinline__ void pv(const char* st, const int (&voff)[4], const bf16x8 (&p)[4]) {
-    bf16x8 vf[4 * OT];
+  // O^T += V^T P^T.  The A operand of k-step kk for O^T rows 32t..32t+31 is
+  // read from the natural V tile with two transposed reads: keys
+  // 16kk + 4h + 0..3 and 16kk + 8 + 4h + 0..3 at head dim 32t + col, the key
+  // order in which the S^T result layout hands out P (see pack_p).
+  __device__ __forceinline__ void pv(const char* st, const int (&vbase)[OT],
+                                     const bf16x8 (&p)[4]) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int t = 0; t < OT; ++t)
-        vf[kk * OT + t] = *reinterpret_cast<const bf16x8*>(st + voff[kk] + t * 32 * Gm::VROW);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int t = 0; t < OT; ++t)
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk * OT + t], p[kk], o[t], 0, 0, 0);
+      for (int t = 0; t < OT; ++t) {
+        const char* a0 = st + vbase[t] + (16 * kk) * Gm::ROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0 + 8 * Gm::ROW));
+        const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
+                                                              hi[0], hi[1], hi[2], hi[3]};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), p[kk],
+                                                       o[t], 0, 0, 0);
+      }
   }
 
   // One whole tile without cross-tile pipelining.
   template <typename Vis>
   __device__ __forceinline__ void tile(const char* st, const int (&koff)[KS],
-                                       const int (&voff)[4], const bf16x8 (&qb)[KS], bool mask,
+                                       const int (&vbase)[OT], const bf16x8 (&qb)[KS], bool mask,
                                        Vis vis) {
     f32x16 s0, s1, n0, n1;
     bf16x8 p[4];
     scores(st, koff, qb, s0, s1);
     head(s0, s1, mask, vis);
     probs<false>(s0, s1, p, st, koff, qb, n0, n1);
-    pv(st, voff, p);
+    pv(st, vbase, p);
   }
 
   // Row sum over both lane halves (call once, all lanes).
   __device__ __forceinline__ float total() const { return l + __shfl_xor(l, 32); }
 };
 
-// This lane's fragment offsets inside a stage (see Flash::tile).
+// This lane's fragment offsets inside a stage (see Flash::scores / pv).
+// koff[ks]: K row col, logical chunk 2ks + hh.  vbase[t]: the address this
+// lane presents to the transposed V read for O^T rows 32t..: row 4h + q
+// (q = (lane % 16) / 4), head dims 32t + 16 ((lane / 16) % 2) + 4 (lane % 4).
 template <int D>
-__device__ __forceinline__ void lane_offsets(int col, int hh, int (&koff)[D / 16], int (&voff)[4]) {
+__device__ __forceinline__ void lane_offsets(int lane, int (&koff)[D / 16], int (&vbase)[D / 32]) {
   using Gm = TileGeom<D>;
+  const int col = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = col * Gm::KROW + Gm::k_phys(col, 2 * ks + hh) * 16;
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = col * Gm::ROW + Gm::k_phys(col, 2 * ks + hh) * 16;
+  const int q = (lane & 15) >> 2, b = (lane >> 4) & 1;
+  const int row = 4 * hh + q;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    voff[kk] = Gm::KBYTES + col * Gm::VROW + Gm::v_phys(col, 2 * kk + hh) * 16;
+  for (int t = 0; t < D / 32; ++t) {
+    const int elem = 32 * t + 16 * b + 4 * (lane & 3);
+    vbase[t] = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, elem >> 3) * 16 + (elem & 7) * 2;
+  }
 }
 
 // Asynchronous copy of `chunks` 16-byte chunks (a multiple of 64 per wave
 // step) from global memory to LDS, bypassing registers: wavefront w moves
 // chunks [64 i, 64 i + 64) for i = w, w + nw, ...; lane L lands at +16 L.
+// Direct global->LDS load of 16 bytes per lane: lane L's bytes land at
+// lds_dst + 16 L (lds_dst wave-uniform).  Written as inline asm on purpose:
+// for the builtin form the compiler cannot tell ring stages apart and puts a
+// wait for every in-flight tile load before later transposing LDS reads,
+// which would drain the prefetch ring each tile.  The callers order LDS
+// accesses themselves (explicit vmcnt waits, then a barrier).  M0 holds the
+// LDS base (set by the compiler from the operand); one wait state separates
+// its write from the load.
+__device__ __forceinline__ void dma16(const void* gsrc, const void* lds_dst) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)lds_dst));
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "{m0}"(base)
+      : "memory");
+}
+
 __device__ __forceinline__ void copy_to_lds(const u32x4* src, char* dst, int chunks, int wave,
                                             int nw, int lane) {
-  for (int i = wave; i * 64 < chunks; i += nw)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(src + i * 64 + lane),
-        (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+  for (int i = wave; i * 64 < chunks; i += nw) dma16(src + i * 64 + lane, dst + i * 1024);
+}
+
+// s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7 = no wait),
+// lgkmcnt 11:8 (15 = no wait).
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
 }
 
 // Wait until at most n of this wave's vector-memory loads are outstanding
-// (n: 0..15, wave-uniform).  Loads complete in issue order, so this waits for
-// all but the n most recent.
+// (wave-uniform n in {0, 2, 4, 8, 12, 16, 24, 32}); loads complete in issue
+// order, so this waits for all but the n most recent.  LGKM0 additionally
+// waits for this wave's LDS operations.
+template <bool LGKM0 = false>
 __device__ __forceinline__ void wait_vm(int n) {
-  // s_waitcnt immediate: vmcnt in bits 3:0, expcnt 6:4 (7 = no wait), lgkmcnt 11:8 (15).
+  constexpr int L = LGKM0 ? 0 : 15;
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 2: waitcnt<2, L>(); break;
+    case 4: waitcnt<4, L>(); break;
+    case 8: waitcnt<8, L>(); break;
+    case 12: waitcnt<12, L>(); break;
+    case 16: waitcnt<16, L>(); break;
+    case 24: waitcnt<24, L>(); break;
+    case 32: waitcnt<32, L>(); break;
+    default: waitcnt<0, L>(); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Flash-attention state for 16 query rows per wavefront on
+// v_mfma_f32_16x16x32_bf16 (used where rows are few: Stage 2).
+//
+// Lane l owns query row l % 16; its group q = l / 16 holds keys 16j + 4q + i
+// (i = 0..3) of every 16-key subtile j of a 64-key tile (the S^T = K Q^T
+// result layout).  O^T += V^T P^T keeps the output in the same layout:
+// o[t][i] is head dim 16t + 4q + i.  Scores carry scale * log2(e), arrive
+// relative to the reference m and use the same lazy raise as Flash.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Flash16 {
+  static constexpr int KS = D / 32;  // k-steps over the head dim
+  static constexpr int OT = D / 16;  // O^T row tiles
+  using Gm = TileGeom<D>;
+  f32x4 o[OT];
+  float m, l;
+  bool have;
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int t = 0; t < OT; ++t) o[t] = f32x4{};
+    m = 0.0f;
+    l = 0.0f;
+    have = false;
+  }
+
+  // One 64-key tile.  koff[ks]: K row l%16, chunk 4ks + q.  vbase[t]: the
+  // transposed V read address for O^T rows 16t.. (row 4q + (l%16)/4).
+  template <typename Vis>
+  __device__ __forceinline__ void tile(const char* st, const int (&koff)[KS],
+                                       const int (&vbase)[OT], const bf16x8 (&qb)[KS], bool mask,
+                                       Vis vis) {
+    f32x4 s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = f32x4{-m, -m, -m, -m};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 16 * j * Gm::ROW);
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], s[j], 0, 0, 0);
+      }
+    const int q = (threadIdx.x >> 4) & 3;
+    if (mask) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[j][i] = vis(16 * j + 4 * q + i) ? s[j][i] : kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(s[j][0], s[j][1]),
+                                               __builtin_fmaxf(s[j][2], s[j][3])));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > kLazy || (!have && mx > kNegInf);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float delta = need ? mx : 0.0f;
+      const float alpha = have ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
+      m += delta;
+      have = have || mx > kNegInf;
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[j][i] -= delta;
+#pragma unroll
+      for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= alpha;
+    }
+    float rs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[j][i] = __builtin_amdgcn_exp2f(s[j][i]);
+        rs += s[j][i];
+      }
+    l += rs;
+    // k-step kk (32 keys): positions 8q + r <-> keys 32kk + 16 (r/4) + 4q + r%4.
+    bf16x8 p[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 w = u32x4{pack_bf16x2(s[2 * kk][0], s[2 * kk][1]),
+                            pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
+                            pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
+                            pack_bf16x2(s[2 * kk + 1][2], s[2 * kk + 1][3])};
+      p[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int t = 0; t < OT; ++t) {
+        const char* a0 = st + vbase[t] + (32 * kk) * Gm::ROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0 + 16 * Gm::ROW));
+        const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
+                                                              hi[0], hi[1], hi[2], hi[3]};
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), p[kk],
+                                                       o[t], 0, 0, 0);
+      }
+  }
+
+  // Row sum over the four lane groups (call once, all lanes).
+  __device__ __forceinline__ float total() const {
+    float t = l + __shfl_xor(l, 16);
+    return t + __shfl_xor(t, 32);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void lane_offsets16(int lane, int (&koff)[D / 32], int (&vbase)[D / 16]) {
+  using Gm = TileGeom<D>;
+  const int r16 = lane & 15, q = (lane >> 4) & 3;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) koff[ks] = r16 * Gm::ROW + Gm::k_phys(r16, 4 * ks + q) * 16;
+  const int row = 4 * q + (r16 >> 2);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const int elem = 16 * t + 4 * (lane & 3);
+    vbase[t] = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, elem >> 3) * 16 + (elem & 7) * 2;
   }
 }
 

@@ -185,7 +185,7 @@ struct Stage1Plan {
   int32_t row0 = 0, row1 = 0;
   int32_t sink_tiles = 0, win_tile0 = 0, win_tile1 = 0, n_slots = 0;
   // workspace layout
-  size_t off_meta = 0, off_k = 0, off_v = 0, total = 0;
+  size_t off_meta = 0, off_k = 0, total = 0;
   size_t meta_bytes = 0;
 };
 
@@ -211,8 +211,6 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
     const size_t tile = (size_t)kKeyTile * a->head_dim * 2;
     p.off_k = cur;
     cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
-    p.off_v = cur;
-    cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
   }
   p.total = cur;
 }
@@ -237,6 +235,8 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   pa.hq = a->n_q_heads;
   pa.hkv = a->n_kv_heads;
   pa.n_qtiles = (int32_t)cdiv(p.row1 - p.row0, kPrefillRows);
+  pa.n_keys = p.n_tokens;
+  pa.v = v;
   pa.sink_tiles = p.sink_tiles;
   pa.win_tile0 = p.win_tile0;
   pa.n_slots = p.n_slots;
@@ -245,9 +245,7 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   if (a->dtype == DBSA_BF16) {
     PackArgs ka;
     ka.k = k;
-    ka.v = v;
     ka.k_tiles = w + p.off_k;
-    ka.v_tiles = w + p.off_v;
     ka.n_tokens = p.n_tokens;
     ka.hkv = a->n_kv_heads;
     ka.sink_tiles = p.sink_tiles;
@@ -258,10 +256,8 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
     hipError_t e = launch_pack(ka, a->head_dim, a->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "launch k_pack");
     pa.k_tiles = ka.k_tiles;
-    pa.v_tiles = ka.v_tiles;
   } else {
     pa.k_tiles = k;  // f32 rows kernel reads the unrotated pool directly
-    pa.v_tiles = v;
   }
   hipError_t e = launch_prefill(pa, a->head_dim, a->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "launch prefill");
@@ -278,21 +274,28 @@ struct SegPlan {
 };
 
 struct QueryPlan {
-  int32_t rows = 0, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  int32_t rows = 0, waves = 8, row_groups = 0, n_split = 1, tiles_per_split = 1;
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
-void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max_ctx,
+void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max_ctx, bool fused,
                  QueryPlan& qp) {
   const int G = a->n_q_heads / a->n_kv_heads;
   qp.rows = n_new * G;
-  qp.row_groups = (int32_t)cdiv(qp.rows, 256);
+  // 16 packed rows per wavefront; 2, 4, 8 or 16 wavefronts per workgroup.
+  // The fused gather keeps RoPE frequencies in registers and would spill at
+  // 16 wavefronts (128 VGPRs each) for head_dim 128, so it stops at 8.
+  qp.waves = qp.rows <= 32 ? 2 : qp.rows <= 64 ? 4 : qp.rows <= 128 ? 8 : 16;
+  if (fused && a->head_dim == 128) qp.waves = std::min(qp.waves, 8);
+  qp.row_groups = (int32_t)cdiv(qp.rows, 16 * qp.waves);
   const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
   qp.n_split = 1;
   qp.tiles_per_split = (int32_t)n_tiles;
   if (a->dtype == DBSA_BF16) {
+    // One workgroup per CU fits (the LDS ring is 128 KiB): aim for ~256 of
+    // them, never fewer than 4 tiles per split.
     const int64_t base = (int64_t)batch * a->n_kv_heads * qp.row_groups;
-    const int64_t want = std::max<int64_t>(1, cdiv(512, base));
+    const int64_t want = std::max<int64_t>(1, cdiv(256, base));
     const int64_t by_len = std::max<int64_t>(1, n_tiles / 4);
     const int64_t ns = std::min(want, by_len);
     qp.tiles_per_split = (int32_t)cdiv(n_tiles, ns);
@@ -372,6 +375,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.hq = a->n_q_heads;
   qa.hkv = a->n_kv_heads;
   qa.rows = qp.rows;
+  qa.waves = qp.waves;
   qa.row_groups = qp.row_groups;
   qa.n_split = qp.n_split;
   qa.tiles_per_split = qp.tiles_per_split;
@@ -524,7 +528,7 @@ size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t
       }
       const int32_t stride = op == DBSA_OP_QUERY ? 2 : n_ids + 2;
       QueryPlan qp;
-      query_split(attn, batch, (int32_t)rows, max_ctx, qp);
+      query_split(attn, batch, (int32_t)rows, max_ctx, op == DBSA_OP_QUERY_GATHERED, qp);
       query_layout(attn, batch, seg_meta_ints(batch, stride), qp);
       if (check_meta(qp.meta_bytes)) return 0;
       return qp.total;
@@ -638,7 +642,7 @@ int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const
   }
   if (max_ctx >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
   QueryPlan qp;
-  query_split(attn, batch, n_new, max_ctx, qp);
+  query_split(attn, batch, n_new, max_ctx, false, qp);
   SegPlan sp;
   seg_init(sp, batch, 2);
   query_layout(attn, batch, sp.tables.size(), qp);
@@ -679,6 +683,9 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
   rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
                   "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
   if (rc) return rc;
+  if (n_ids + 1 > kMaxSegments)
+    return fail(DBSA_EUNSUPPORTED, "n_ids %d exceeds the %d supported blocks per query", n_ids,
+                kMaxSegments - 1);
   const int32_t stride = n_ids + 2;
   SegPlan sp;
   seg_init(sp, batch, stride);
@@ -709,7 +716,7 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
     max_ctx = std::max(max_ctx, total);
   }
   QueryPlan qp;
-  query_split(attn, batch, n_new, max_ctx, qp);
+  query_split(attn, batch, n_new, max_ctx, true, qp);
   query_layout(attn, batch, sp.tables.size(), qp);
   rc = check_meta(qp.meta_bytes);
   if (!rc) rc = check_ws(ws, ws_bytes, qp.total);

@@ -17,7 +17,7 @@ constexpr int kRowsPerWave = 32;  // query rows per wavefront (MFMA N dimension)
 constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
 constexpr int kPrefillStages = 4;  // LDS ring of K/V tiles (3 tiles of lookahead)
-constexpr int kQueryMaxWaves = 8;  // waves per Stage-2 workgroup (<= 256 packed rows)
+constexpr int kMaxSegments = 512;  // context segments per batch row in Stage 2
 constexpr int kMaxHalf = 64;       // head_dim / 2 upper bound (head_dim <= 128)
 
 // RoPE frequencies in revolutions per position: w_i / (2 pi), w_i = theta^(-2i/d),
@@ -27,15 +27,13 @@ struct RopeFreq {
 };
 
 // ---------------------------------------------------------------------------
-// Stage 1: K rotation + V transpose into MFMA-ready tiles.
+// Stage 1: K rotation into MFMA-ready tile images.
 // ---------------------------------------------------------------------------
 // Key tiles are the 64-token tiles of the pool.  Only tiles in [0, sink_tiles)
 // and [win_tile0, win_tile1) are materialised; slot(kt) maps them densely.
 struct PackArgs {
   const void* k;        // [n_tokens][hkv][d] unrotated
-  const void* v;        // [n_tokens][hkv][d]
   void* k_tiles;        // [hkv][n_slots][64][d] rotated, LDS byte image
-  void* v_tiles;        // [hkv][n_slots][d][64] transposed, LDS byte image
   int32_t n_tokens;     // keys beyond are zero-filled
   int32_t hkv;
   int32_t sink_tiles;   // tiles [0, sink_tiles) materialised
@@ -48,7 +46,7 @@ struct PackArgs {
 struct PrefillArgs {
   const void* q;            // [n_tokens][hq][d] unrotated (rows of this call)
   const void* k_tiles;      // from PackArgs
-  const void* v_tiles;
+  const void* v;            // [n_keys][hkv][d] values (natural layout, read directly)
   void* o;                  // [rows][hq][d]
   const int32_t* offsets;   // device int32[n_blocks + 1], block start tokens
   int32_t n_blocks;
@@ -57,7 +55,8 @@ struct PrefillArgs {
   int32_t row0, row1;       // absolute query rows [row0, row1) of this call
   int32_t q_row0;           // absolute row of q[0] / o[0]
   int32_t hq, hkv;
-  int32_t n_qtiles;         // ceil((row1 - row0) / 128)
+  int32_t n_qtiles;         // ceil((row1 - row0) / kPrefillRows)
+  int32_t n_keys;           // keys available (rows of v)
   int32_t sink_tiles, win_tile0, n_slots;  // key-tile slot map (see PackArgs)
   float q_scale;            // softmax scale * log2(e), folded into Q
   RopeFreq freq;
@@ -116,7 +115,8 @@ struct QueryArgs {
   const int32_t* pos0;    // [batch] position of new token 0 (= keys before it)
   int32_t n_new, hq, hkv;
   int32_t rows;           // n_new * (hq / hkv) packed rows per kv head
-  int32_t row_groups;     // ceil(rows / 256)
+  int32_t waves;          // wavefronts per workgroup (2, 4, 8 or 16): 16 rows each
+  int32_t row_groups;     // ceil(rows / (16 * waves))
   int32_t n_split;        // key splits per (batch, kv head, row group)
   int32_t tiles_per_split;
   int64_t cap;

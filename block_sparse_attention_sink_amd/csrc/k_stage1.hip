@@ -19,55 +19,28 @@
 namespace dbsa {
 
 // ---------------------------------------------------------------------------
-// K rotation + V transpose into tile images (the LDS byte images, see TileGeom).
+// K rotation into tile images (the LDS byte images, see TileGeom).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
+  using Gm = TileGeom<D>;
   constexpr int CP = D / 16;  // chunk pairs per key row (first half / second half)
   constexpr int CR = D / 8;   // 16-byte chunks per key row
-  constexpr int NT = 64 * CP;
-  __shared__ __align__(16) uint16_t vs[64][D + 8];
-
   const int slot = blockIdx.x, g = blockIdx.y;
   const int kt = slot < a.sink_tiles ? slot : a.win_tile0 + (slot - a.sink_tiles);
   const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
   const int64_t tok = (int64_t)kt * kKeyTile + key;
-
-  u32x4 k1 = u32x4{0u, 0u, 0u, 0u}, k2 = k1, v1 = k1, v2 = k1;
+  u32x4 k1 = u32x4{0u, 0u, 0u, 0u}, k2 = k1;
   if (tok < a.n_tokens) {
-    const int64_t row = (tok * a.hkv + g) * D;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + row);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + row);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) +
+                                                     (tok * a.hkv + g) * D);
     k1 = kp[c];
     k2 = kp[c + CP];
-    v1 = vp[c];
-    v2 = vp[c + CP];
     rope_rotate_chunk(k1, k2, tok, a.freq, 8 * c);
   }
-  const int64_t tile = (int64_t)g * a.n_slots + slot;
-  u32x4* ko = reinterpret_cast<u32x4*>(a.k_tiles) + tile * (64 * CR);
-  using Gm = TileGeom<D>;
+  u32x4* ko = reinterpret_cast<u32x4*>(a.k_tiles) + ((int64_t)g * a.n_slots + slot) * (64 * CR);
   ko[key * CR + Gm::k_phys(key, c)] = k1;
   ko[key * CR + Gm::k_phys(key, c + CP)] = k2;
-
-  *reinterpret_cast<u32x4*>(&vs[key][8 * c]) = v1;
-  *reinterpret_cast<u32x4*>(&vs[key][D / 2 + 8 * c]) = v2;
-  __syncthreads();
-
-  u32x4* vo = reinterpret_cast<u32x4*>(a.v_tiles) + tile * (D * 8);
-  for (int u = tid; u < D * 8; u += NT) {
-    const int drow = u >> 3, ch = u & 7;
-    const int kbase = 16 * (ch >> 1);
-    uint32_t w[4];
-#pragma unroll
-    for (int r = 0; r < 8; r += 2) {
-      const int p = 8 * (ch & 1) + r;
-      const uint32_t lo = vs[kbase + vt_key_of_pos(p)][drow];
-      const uint32_t hi = vs[kbase + vt_key_of_pos(p + 1)][drow];
-      w[r >> 1] = lo | (hi << 16);
-    }
-    vo[drow * 8 + Gm::v_phys(drow, ch)] = u32x4{w[0], w[1], w[2], w[3]};
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -136,20 +109,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   fl.init();
 
   const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
-  const u32x4* vbase = reinterpret_cast<const u32x4*>(a.v_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
   auto tile_of = [&](int it) { return it < nsink ? it : win0 + (it - nsink); };
   auto slot_of = [&](int kt) {
     return kt < a.sink_tiles ? kt : a.sink_tiles + (kt - a.win_tile0);
   };
-  // Stage tile `it` into LDS stage `buf` (K image then V^T image), no registers.
+  // Stage tile `it` into LDS stage `buf` without registers: the K image is a
+  // linear copy; V rows come straight from the token-major tensor, each lane
+  // fetching the chunk that belongs at its LDS position.
   auto load = [&](int it, int buf) {
-    const int64_t sl = (int64_t)slot_of(tile_of(it)) * Gm::TU4;
+    const int kt = tile_of(it);
     char* st = lds + buf * Gm::STAGE;
-    copy_to_lds(kbase + sl, st, Gm::TU4, wave, kPrefillWaves, lane);
-    copy_to_lds(vbase + sl, st + Gm::KBYTES, Gm::TU4, wave, kPrefillWaves, lane);
+    copy_to_lds(kbase + (int64_t)slot_of(kt) * Gm::TU4, st, Gm::TU4, wave, kPrefillWaves, lane);
+    for (int i = wave; i * 64 < Gm::TU4; i += kPrefillWaves) {
+      const int off = i * 1024 + lane * 16;
+      const int row = off / Gm::ROW, c = Gm::v_phys(row, (off % Gm::ROW) >> 4);
+      const int64_t tok = min(kt * kKeyTile + row, a.n_keys - 1);
+      dma16(vsrc + (tok * a.hkv + g) * D + c * 8, st + Gm::KBYTES + i * 1024);
+    }
   };
-  int koff[KS], voff[4];
-  lane_offsets<D>(col, hh, koff, voff);
+  int koff[KS], vbase[D / 32];
+  lane_offsets<D>(lane, koff, vbase);
 
   // Ring of NST stages: tile it+NST-1 is requested while tile it is computed.
   for (int p = 0; p < NST - 1 && p < n_tiles; ++p) load(p, p);
@@ -165,7 +145,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     const bool full = (k0 + kKeyTile - 1 <= r0) &&
                       (k0 >= lo_last || (a.sink && k0 + kKeyTile <= sink_end));
     const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
-    fl.tile(lds + (it % NST) * Gm::STAGE, koff, voff, qb, !full,
+    fl.tile(lds + (it % NST) * Gm::STAGE, koff, vbase, qb, !full,
             [=](int kr) { return kr <= tt && (kr >= lt || kr < se); });
   }
 
@@ -252,7 +232,7 @@ __global__ __launch_bounds__(256) void k_rows_f32(PrefillArgs a) {
   const int sink_end = a.sink ? off[1] : 0;
   const int lo_t = off[max(upper_index(off, a.n_blocks, t) - a.j, 0)];
   const float* k = static_cast<const float*>(a.k_tiles) + (int64_t)g * D;
-  const float* v = static_cast<const float*>(a.v_tiles) + (int64_t)g * D;
+  const float* v = static_cast<const float*>(a.v) + (int64_t)g * D;
   const int64_t stride = (int64_t)a.hkv * D;
   float m_run = kMaxFloor, l_run = 0.0f, acc[2] = {0.0f, 0.0f};
   if (a.sink && lo_t > 0) rows_f32_chunk<D>(qr, k, v, stride, 0, sink_end, m_run, l_run, acc, a.freq, lane);

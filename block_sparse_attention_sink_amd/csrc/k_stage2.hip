@@ -134,26 +134,38 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
-// Workgroup = 8 wavefronts over 256 packed rows (row = token * G + head in
-// group) of one KV head; every wavefront also stages its share of each 64-key
-// K/V tile.  Lane layout and the softmax follow the prefill kernel.
+// Workgroup = NW wavefronts over 16 NW packed rows (row = token * G + head in
+// group) of one KV head and one key split (16 rows per wavefront on
+// v_mfma_f32_16x16x32_bf16, see Flash16).  Each 64-key tile is staged by
+// direct global->LDS loads through a ring of 4 stages, three tiles ahead:
+// per tile, 64 threads first resolve every row's source (segment lookup in
+// LDS: pool block, rotated on load, or the row's own context buffer) into a
+// small address table, then all waves issue the loads.  FUSED rotates the K
+// rows that come from the pool in LDS, at their gathered position, before
+// the tile is used.  Lane layout and softmax: see Flash.
 // ---------------------------------------------------------------------------
-template <int D, bool FUSED>
-__global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
+template <int D, int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
-  constexpr int KS = D / 16, CP = D / 16;
-  constexpr int UNITS = 64 * CP;         // (key, chunk pair) units per tile
-  constexpr int UPT = (UNITS + 511) / 512;
-  __shared__ __align__(16) char lds[2 * Gm::STAGE];
+  constexpr int KS = D / 32, OT = D / 16, CP = D / 16, CR = D / 8;
+  constexpr int RW = 16;  // rows per wavefront
+  constexpr int NST = 4;
+  constexpr int INSTR = Gm::TU4 / 64;  // 1 KiB loads per matrix per tile
+  constexpr int LPW = 2 * INSTR / NW;  // loads per wave per tile
+  static_assert((2 * INSTR) % NW == 0, "loads must split evenly over the waves");
+  __shared__ __align__(16) char lds[NST * Gm::STAGE];
+  __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
+  __shared__ uint64_t row_k[NST][kKeyTile], row_v[NST][kKeyTile];
+  __shared__ uint8_t row_rot[NST][kKeyTile];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hh = lane >> 5, col = lane & 31;
+  const int q16 = (lane >> 4) & 3, r16 = lane & 15;
   const int split = blockIdx.x;
   const int g = blockIdx.y % a.hkv, rg = blockIdx.y / a.hkv, b = blockIdx.z;
   const int G = a.hq / a.hkv;
-  const int wrow0 = rg * 256 + wave * kRowsPerWave;
+  const int wrow0 = rg * (RW * NW) + wave * RW;
   const bool wave_live = wrow0 < a.rows;
-  const int rho = wrow0 + col;
+  const int rho = wrow0 + r16;
   const bool live = rho < a.rows;
   const int r = live ? rho / G : 0;
   const int head = g * G + (live ? rho - (rho / G) * G : 0);
@@ -161,13 +173,13 @@ __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
   const int qpos = pos0 + r;
 
   const int nseg = a.seg.nseg[b];
-  const int32_t* sst = a.seg.start + (int64_t)b * a.seg.seg_stride;
-  const int32_t* ssrc = a.seg.src + (int64_t)b * a.seg.seg_stride;
-  const int32_t* sbuf = a.seg.buf + (int64_t)b * a.seg.seg_stride;
-  const int T = sst[nseg];
-  const int n_tiles = (T + kKeyTile - 1) / kKeyTile;
-  const int it0 = split * a.tiles_per_split;
-  const int it1 = min(it0 + a.tiles_per_split, n_tiles);
+  for (int i = tid; i <= nseg; i += 64 * NW) {
+    seg_start[i] = a.seg.start[(int64_t)b * a.seg.seg_stride + i];
+    if (i < nseg) {
+      seg_src[i] = a.seg.src[(int64_t)b * a.seg.seg_stride + i];
+      seg_buf[i] = a.seg.buf[(int64_t)b * a.seg.seg_stride + i];
+    }
+  }
 
   bf16x8 qb[KS];
   {
@@ -175,135 +187,135 @@ __global__ __launch_bounds__(512) void k_query_bf16(QueryArgs a) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.n_new + r) * a.hq + head) * D);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[4 * ks + q16] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], qpos, a.freq, 16 * ks + 8 * hh, a.q_scale);
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], qpos, a.freq, 32 * ks + 8 * q16, a.q_scale);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
+  __syncthreads();  // segment table visible; Q loads retired
 
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-  const uint16_t* kctx = static_cast<const uint16_t*>(a.k_ctx);
-  const uint16_t* vctx = static_cast<const uint16_t*>(a.v_ctx);
+  const int T = seg_start[nseg];
+  const int n_tiles = (T + kKeyTile - 1) / kKeyTile;
+  const int it0 = split * a.tiles_per_split;
+  const int cnt = max(0, min(it0 + a.tiles_per_split, n_tiles) - it0);
 
-  // Staging registers of one tile: this thread's (key, chunk pair) units.
-  u32x4 k1[UPT], k2[UPT], v1[UPT], v2[UPT];
-  int upos[UPT];
-  bool urot[UPT];
+  const uint64_t kpool_u = reinterpret_cast<uint64_t>(a.k_pool);
+  const uint64_t vpool_u = reinterpret_cast<uint64_t>(a.v_pool);
+  const uint64_t kctx_u = reinterpret_cast<uint64_t>(a.k_ctx);
+  const uint64_t vctx_u = reinterpret_cast<uint64_t>(a.v_ctx);
 
-  auto fetch = [&](int it) {
-    const int u0 = it * kKeyTile;
-#pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int unit = tid + 512 * x;
-      const int key = unit / CP, c = unit - key * CP;
-      const int u = u0 + key;
-      upos[x] = u;
-      urot[x] = false;
-      k1[x] = k2[x] = v1[x] = v2[x] = u32x4{0u, 0u, 0u, 0u};
-      if (unit < UNITS && u < T) {
-        const int s = upper_index(sst, nseg, u);
-        const int64_t tok = ssrc[s] + (u - sst[s]);
-        const uint16_t* kr;
-        const uint16_t* vr;
-        if (FUSED && sbuf[s] == 0) {
-          kr = kpool + (tok * a.hkv + g) * D;
-          vr = vpool + (tok * a.hkv + g) * D;
-          urot[x] = true;
-        } else {
-          const int64_t row = (((int64_t)b * a.cap + tok) * a.hkv + g) * D;
-          kr = kctx + row;
-          vr = vctx + row;
-        }
-        const u32x4* kq = reinterpret_cast<const u32x4*>(kr);
-        const u32x4* vq = reinterpret_cast<const u32x4*>(vr);
-        k1[x] = kq[c];
-        k2[x] = kq[c + CP];
-        v1[x] = vq[c];
-        v2[x] = vq[c + CP];
-      }
+  // Row sources of local tile li (threads 0..63, one row each).
+  auto plan = [&](int li) {
+    if (tid < kKeyTile) {
+      const int u_real = (it0 + li) * kKeyTile + tid;
+      const int u = min(u_real, T - 1);  // rows past the context repeat the last row (masked)
+      const int s = upper_index(seg_start, nseg, u);
+      const int64_t tok = seg_src[s] + (u - seg_start[s]);
+      const bool pool = FUSED && seg_buf[s] == 0;
+      // Branch-free select of the source tensor (a pointer select here is
+      // otherwise lowered to a lookup table in scratch memory).
+      const uint64_t m = pool ? ~0ull : 0ull;
+      const uint64_t off =
+          2ull * static_cast<uint64_t>(((pool ? 0 : (int64_t)b * a.cap) + tok) * a.hkv + g) * D;
+      const int slot = li % NST;
+      row_k[slot][tid] = ((kpool_u & m) | (kctx_u & ~m)) + off;
+      row_v[slot][tid] = ((vpool_u & m) | (vctx_u & ~m)) + off;
+      row_rot[slot][tid] = pool && u_real < T;
     }
   };
-  // Rotate (pool tokens), then write K rows and V^T columns into a stage.
-  auto stage = [&](int buf) {
-    char* st = lds + buf * Gm::STAGE;
+  // Loads of local tile li into its stage (all waves).
+  auto load = [&](int li) {
+    const int slot = li % NST;
+    char* st = lds + slot * Gm::STAGE;
+    const uint16_t* src[LPW];
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int unit = tid + 512 * x;
-      if (unit >= UNITS) continue;
-      const int key = unit / CP, c = unit - key * CP;
-      if (FUSED && urot[x]) rope_rotate_chunk(k1[x], k2[x], upos[x], a.freq, 8 * c);
-      *reinterpret_cast<u32x4*>(st + key * Gm::KROW + Gm::k_phys(key, c) * 16) = k1[x];
-      *reinterpret_cast<u32x4*>(st + key * Gm::KROW + Gm::k_phys(key, c + CP) * 16) = k2[x];
-      // V^T: head dim d of this key goes to row d, chunk ch, element e.
-      const int p = vt_pos_of_key(key & 15);
-      const int ch = 2 * (key >> 4) + (p >> 3), e = p & 7;
-      char* vt = st + Gm::KBYTES + e * 2;
-      const uint32_t w1[4] = {v1[x].x, v1[x].y, v1[x].z, v1[x].w};
-      const uint32_t w2[4] = {v2[x].x, v2[x].y, v2[x].z, v2[x].w};
+    for (int j = 0; j < LPW; ++j) {
+      const int i = wave + j * NW;  // 0 .. 2*INSTR-1
+      const int mat = i / INSTR, ii = i - mat * INSTR;
+      const int off = ii * 1024 + lane * 16;
+      const int row = off / Gm::ROW, p = (off % Gm::ROW) >> 4;
+      const int c = mat == 0 ? Gm::k_phys(row, p) : Gm::v_phys(row, p);
+      src[j] = reinterpret_cast<const uint16_t*>(mat == 0 ? row_k[slot][row] : row_v[slot][row]) +
+               c * 8;
+    }
+    // All table reads first, then the loads back to back.
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int d1 = 8 * c + q, d2 = D / 2 + 8 * c + q;
-        *reinterpret_cast<uint16_t*>(vt + d1 * Gm::VROW + Gm::v_phys(d1, ch) * 16) =
-            (uint16_t)(q & 1 ? w1[q >> 1] >> 16 : w1[q >> 1]);
-        *reinterpret_cast<uint16_t*>(vt + d2 * Gm::VROW + Gm::v_phys(d2, ch) * 16) =
-            (uint16_t)(q & 1 ? w2[q >> 1] >> 16 : w2[q >> 1]);
-      }
+    for (int j = 0; j < LPW; ++j) {
+      const int i = wave + j * NW;
+      const int mat = i / INSTR, ii = i - mat * INSTR;
+      dma16(src[j], st + mat * Gm::KBYTES + ii * 1024);
     }
   };
 
-  Flash<D> fl;
+  Flash16<D> fl;
   fl.init();
-  int koff[KS], voff[4];
-  lane_offsets<D>(col, hh, koff, voff);
-
-  if (it0 < it1) {
-    fetch(it0);
-    stage(0);
+  int koff[KS], vbase[OT];
+  lane_offsets16<D>(lane, koff, vbase);
+  // The in-LDS rotation handles chunk pair tid % CP of its rows: its 8
+  // frequencies live in registers (no per-lane kernel-argument loads in the
+  // loop, whose vector-memory counter is reserved for the tile loads).
+  double fr[8];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (tid % CP) + i];
   }
-  __syncthreads();
-  for (int it = it0; it < it1; ++it) {
-    const int cur = (it - it0) & 1;
-    if (it + 1 < it1) fetch(it + 1);
-    if (wave_live) {
-      const char* st = lds + cur * Gm::STAGE;
-      const int u0 = it * kKeyTile;
-      const int lim = qpos - u0;  // keys kr <= lim are visible (causal over new tokens)
-      fl.tile(st, koff, voff, qb, u0 + kKeyTile - 1 > pos0, [=](int kr) { return kr <= lim; });
+
+  for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
+  waitcnt<0, 0>();
+  barrier_nofence();
+  for (int li = 0; li < NST - 1 && li < cnt; ++li) load(li);
+  for (int li = 0; li < cnt; ++li) {
+    if (li + NST - 1 < cnt) plan(li + NST - 1);
+    // Tile li landed (only the younger tiles' loads may fly); the barrier also
+    // publishes the new address table and frees the stage refilled below.
+    wait_vm<true>(LPW * min(NST - 2, cnt - 1 - li));
+    barrier_nofence();
+    if (li + NST - 1 < cnt) load(li + NST - 1);
+    char* st = lds + (li % NST) * Gm::STAGE;
+    const int u0 = (it0 + li) * kKeyTile;
+    if constexpr (FUSED) {
+      // Re-apply RoPE at the gathered position to the K rows from the pool.
+      static_assert((64 * NW) % CP == 0, "each thread keeps one chunk pair");
+      for (int uidx = tid; uidx < kKeyTile * CP; uidx += 64 * NW) {
+        const int row = uidx / CP, c = uidx - row * CP;
+        if (!row_rot[li % NST][row]) continue;
+        u32x4* k1 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c) * 16);
+        u32x4* k2 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c + CP) * 16);
+        u32x4 x1 = *k1, x2 = *k2;
+        rope_rotate_chunk_f(x1, x2, u0 + row, fr);
+        *k1 = x1;
+        *k2 = x2;
+      }
+      waitcnt<63, 0>();
+      barrier_nofence();
     }
-    if (it + 1 < it1) stage(cur ^ 1);
-    __syncthreads();
+    if (wave_live) {
+      const int lim = qpos - u0;  // keys kr <= lim are visible (causal over new tokens)
+      fl.tile(st, koff, vbase, qb, u0 + kKeyTile - 1 > pos0, [=](int kr) { return kr <= lim; });
+    }
   }
+  (void)CR;
 
-  if (!live) return;
   const float lsum = fl.total();
+  if (!live) return;
   if (a.n_split == 1) {
     const float inv = 1.0f / lsum;
     uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = m * 32 + q4 * 8 + hh * 4;
-        const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
-                         pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
+    for (int t = 0; t < OT; ++t) {
+      const int d = 16 * t + 4 * q16;
+      const u32x2 w = {pack_bf16x2(fl.o[t][0] * inv, fl.o[t][1] * inv),
+                       pack_bf16x2(fl.o[t][2] * inv, fl.o[t][3] * inv)};
+      *reinterpret_cast<u32x2*>(op + d) = w;
+    }
   } else {
     const int64_t prow = (((int64_t)b * a.hkv + g) * a.n_split + split) * a.rows + rho;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = m * 32 + q4 * 8 + hh * 4;
-        *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{fl.o[m][4 * q4 + 0], fl.o[m][4 * q4 + 1], fl.o[m][4 * q4 + 2],
-                  fl.o[m][4 * q4 + 3]};
-      }
-    if (hh == 0) {
+    for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t + 4 * q16) = fl.o[t];
+    if (q16 == 0) {
       a.part_ml[prow * 2 + 0] = fl.m;
       a.part_ml[prow * 2 + 1] = lsum;
     }
@@ -461,6 +473,27 @@ hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
   return hipGetLastError();
 }
 
+template <int D, int NW>
+static void launch_query_nw(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
+  if constexpr (D == 128 && NW == 16) {
+    // The host plans at most 8 wavefronts for the fused form at head_dim 128.
+    hipLaunchKernelGGL((k_query_bf16<D, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+  } else {
+    if (fused) hipLaunchKernelGGL((k_query_bf16<D, NW, true>), grid, dim3(64 * NW), 0, stream, a);
+    else hipLaunchKernelGGL((k_query_bf16<D, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+  }
+}
+
+template <int D>
+static void launch_query_d(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
+  switch (a.waves) {
+    case 2: launch_query_nw<D, 2>(a, grid, fused, stream); break;
+    case 4: launch_query_nw<D, 4>(a, grid, fused, stream); break;
+    case 8: launch_query_nw<D, 8>(a, grid, fused, stream); break;
+    default: launch_query_nw<D, 16>(a, grid, fused, stream); break;
+  }
+}
+
 hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
                         hipStream_t stream) {
   if (dtype == 1) {
@@ -470,14 +503,10 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     return hipGetLastError();
   }
   const bool fused = a.k_pool != nullptr;
+  if (fused && head_dim == 128 && a.waves > 8) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
-  if (head_dim == 128) {
-    if (fused) hipLaunchKernelGGL((k_query_bf16<128, true>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((k_query_bf16<128, false>), grid, dim3(512), 0, stream, a);
-  } else {
-    if (fused) hipLaunchKernelGGL((k_query_bf16<64, true>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((k_query_bf16<64, false>), grid, dim3(512), 0, stream, a);
-  }
+  if (head_dim == 128) launch_query_d<128>(a, grid, fused, stream);
+  else launch_query_d<64>(a, grid, fused, stream);
   return hipGetLastError();
 }
 
