@@ -34,6 +34,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KEY_TILE, ROW_TILE = 64, 256
 PREFILL_PROFILE = os.path.join(ROOT, "profiles", "k_prefill_bf16_llama2_30x1024.md")
+PREFILL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_sink_amd", "csrc", f)
+                   for f in ("k_stage1.hip", "dbsa_device.hpp", "dbsa_internal.hpp")]
 
 
 def visible_pairs(lens, sink, j):
@@ -64,9 +66,17 @@ def executed_tiles(lens, sink, j):
     return tiles
 
 
-def profile_traffic(path, source):
+def source_digest(paths):
+    """sha256 over the concatenated bytes of the kernel's source files."""
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def profile_traffic(path, sources):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel sources."""
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -74,8 +84,7 @@ def profile_traffic(path, source):
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     if not m or not t:
         return None
-    cur = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    return float(t.group(1)) if m.group(1) == cur else None
+    return float(t.group(1)) if m.group(1) == source_digest(sources) else None
 
 
 def cpu_threads():
@@ -199,8 +208,12 @@ def main():
     value = tile_flop / (ms_step * 1e-3) / 1e12
     achieved = exact_flop / (ms_prefill * 1e-3) / 1e12
 
-    # Stage 2 alone, last-level cache flushed between repetitions (1 GiB write).
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # Stage 2 alone, caches flushed between repetitions by reading 1 GiB (a
+    # read leaves clean lines; a write-based flush would leave up to the
+    # last-level cache's size of dirty lines to be written back inside the
+    # timed call).
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     kv_bytes = tp * hkv * d * 2 * 2
     io_bytes = (qn.numel() + kn.numel() + vn.numel() + on.numel()) * 2
     tail_k = torch.empty((1, n_new, hkv, d), dtype=torch.bfloat16, device=dev)
@@ -209,7 +222,7 @@ def main():
     def timed(fn, reps=10):
         ts = []
         for _ in range(reps + 2):
-            flush.zero_()
+            flush_sink.add_(flush.sum())
             a, b = ev(), ev()
             a.record()
             fn()
@@ -235,7 +248,8 @@ def main():
                                "frac_hbm": (kv_bytes + io_bytes) / (f_ms * 1e-3) / 1e9
                                / PEAK_HBM_GBS},
         "note": "algorithmic bytes = unrotated K+V of the gathered tokens read once + Q, new K/V, "
-                "O; gather counts its read and write; cache flushed between repetitions",
+                "O; gather counts its read and write; caches flushed (1 GiB read) between "
+                "repetitions",
     }
 
     cpu = None
@@ -264,8 +278,7 @@ def main():
                          f"x all {hq} heads of the same workload, {secs:.1f} s; value counts the "
                          "exact visible pairs of the sampled rows"}
 
-    traffic = profile_traffic(PREFILL_PROFILE, os.path.join(
-        ROOT, "block_sparse_attention_sink_amd", "csrc", "k_stage1.hip"))
+    traffic = profile_traffic(PREFILL_PROFILE, PREFILL_SOURCES)
     out = {
         "metric": "DBSA prefill TFLOP/s (unmasked tiles) + gather/query-attn GB/s, % roofline",
         "value": value,

@@ -387,13 +387,14 @@ __device__ __forceinline__ void waitcnt() {
 }
 
 // Wait until at most n of this wave's vector-memory loads are outstanding
-// (wave-uniform n in {0, 2, 4, 8, 12, 16, 24, 32}); loads complete in issue
+// (wave-uniform n in {0, 1, 2, 4, 8, 12, 16, 24, 32}); loads complete in issue
 // order, so this waits for all but the n most recent.  LGKM0 additionally
 // waits for this wave's LDS operations.
 template <bool LGKM0 = false>
 __device__ __forceinline__ void wait_vm(int n) {
   constexpr int L = LGKM0 ? 0 : 15;
   switch (n) {
+    case 1: waitcnt<1, L>(); break;
     case 2: waitcnt<2, L>(); break;
     case 4: waitcnt<4, L>(); break;
     case 8: waitcnt<8, L>(); break;
@@ -432,32 +433,36 @@ struct Flash16 {
     have = false;
   }
 
-  // One 64-key tile.  koff[ks]: K row l%16, chunk 4ks + q.  vbase[t]: the
+  // KH keys (64 or 32) of one 64-key tile, starting at the key offset folded
+  // into koff / vbase.  koff[ks]: K row l%16, chunk 4ks + q.  vbase[t]: the
   // transposed V read address for O^T rows 16t.. (row 4q + (l%16)/4).
-  template <typename Vis>
+  // vis(kr) takes the key index relative to that offset.
+  template <int KH, typename Vis>
   __device__ __forceinline__ void tile(const char* st, const int (&koff)[KS],
                                        const int (&vbase)[OT], const bf16x8 (&qb)[KS], bool mask,
                                        Vis vis) {
-    f32x4 s[4];
+    static_assert(KH == 64 || KH == 32, "32 or 64 keys per wavefront");
+    constexpr int NJ = KH / 16, NK = KH / 32;
+    f32x4 s[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = f32x4{-m, -m, -m, -m};
+    for (int j = 0; j < NJ; ++j) s[j] = f32x4{-m, -m, -m, -m};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 16 * j * Gm::ROW);
         s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], s[j], 0, 0, 0);
       }
     const int q = (threadIdx.x >> 4) & 3;
     if (mask) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[j][i] = vis(16 * j + 4 * q + i) ? s[j][i] : kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
       mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(s[j][0], s[j][1]),
                                                __builtin_fmaxf(s[j][2], s[j][3])));
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
@@ -470,7 +475,7 @@ struct Flash16 {
       have = have || mx > kNegInf;
       l *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[j][i] -= delta;
 #pragma unroll
@@ -480,7 +485,7 @@ struct Flash16 {
     }
     float rs = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[j][i] = __builtin_amdgcn_exp2f(s[j][i]);
@@ -488,9 +493,9 @@ struct Flash16 {
       }
     l += rs;
     // k-step kk (32 keys): positions 8q + r <-> keys 32kk + 16 (r/4) + 4q + r%4.
-    bf16x8 p[2];
+    bf16x8 p[NK];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
       const u32x4 w = u32x4{pack_bf16x2(s[2 * kk][0], s[2 * kk][1]),
                             pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
                             pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
@@ -499,7 +504,7 @@ struct Flash16 {
     }
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int t = 0; t < OT; ++t) {
         const char* a0 = st + vbase[t] + (32 * kk) * Gm::ROW;
@@ -521,13 +526,18 @@ struct Flash16 {
   }
 };
 
+// key0 (a multiple of 16) selects the first key of the wavefront's share of
+// the tile; both swizzles depend only on the row modulo 16, so it is a pure
+// row offset.
 template <int D>
-__device__ __forceinline__ void lane_offsets16(int lane, int (&koff)[D / 32], int (&vbase)[D / 16]) {
+__device__ __forceinline__ void lane_offsets16(int lane, int key0, int (&koff)[D / 32],
+                                               int (&vbase)[D / 16]) {
   using Gm = TileGeom<D>;
   const int r16 = lane & 15, q = (lane >> 4) & 3;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) koff[ks] = r16 * Gm::ROW + Gm::k_phys(r16, 4 * ks + q) * 16;
-  const int row = 4 * q + (r16 >> 2);
+  for (int ks = 0; ks < D / 32; ++ks)
+    koff[ks] = (key0 + r16) * Gm::ROW + Gm::k_phys(r16, 4 * ks + q) * 16;
+  const int row = key0 + 4 * q + (r16 >> 2);
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     const int elem = 16 * t + 4 * (lane & 3);

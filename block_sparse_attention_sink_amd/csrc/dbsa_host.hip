@@ -274,7 +274,7 @@ struct SegPlan {
 };
 
 struct QueryPlan {
-  int32_t rows = 0, waves = 8, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  int32_t rows = 0, row_waves = 8, row_groups = 0, n_split = 1, tiles_per_split = 1;
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
@@ -282,12 +282,13 @@ void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max
                  QueryPlan& qp) {
   const int G = a->n_q_heads / a->n_kv_heads;
   qp.rows = n_new * G;
-  // 16 packed rows per wavefront; 2, 4, 8 or 16 wavefronts per workgroup.
+  // 16 packed rows per row wavefront; up to 4 of them split every key tile
+  // between two wavefronts (so 2 .. 8 wavefronts), 8 or 16 take whole tiles.
   // The fused gather keeps RoPE frequencies in registers and would spill at
   // 16 wavefronts (128 VGPRs each) for head_dim 128, so it stops at 8.
-  qp.waves = qp.rows <= 32 ? 2 : qp.rows <= 64 ? 4 : qp.rows <= 128 ? 8 : 16;
-  if (fused && a->head_dim == 128) qp.waves = std::min(qp.waves, 8);
-  qp.row_groups = (int32_t)cdiv(qp.rows, 16 * qp.waves);
+  qp.row_waves = qp.rows <= 16 ? 1 : qp.rows <= 32 ? 2 : qp.rows <= 64 ? 4 : qp.rows <= 128 ? 8 : 16;
+  if (fused && a->head_dim == 128) qp.row_waves = std::min(qp.row_waves, 8);
+  qp.row_groups = (int32_t)cdiv(qp.rows, 16 * qp.row_waves);
   const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
   qp.n_split = 1;
   qp.tiles_per_split = (int32_t)n_tiles;
@@ -375,7 +376,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.hq = a->n_q_heads;
   qa.hkv = a->n_kv_heads;
   qa.rows = qp.rows;
-  qa.waves = qp.waves;
+  qa.row_waves = qp.row_waves;
   qa.row_groups = qp.row_groups;
   qa.n_split = qp.n_split;
   qa.tiles_per_split = qp.tiles_per_split;

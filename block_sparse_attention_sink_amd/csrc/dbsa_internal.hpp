@@ -115,8 +115,8 @@ struct QueryArgs {
   const int32_t* pos0;    // [batch] position of new token 0 (= keys before it)
   int32_t n_new, hq, hkv;
   int32_t rows;           // n_new * (hq / hkv) packed rows per kv head
-  int32_t waves;          // wavefronts per workgroup (2, 4, 8 or 16): 16 rows each
-  int32_t row_groups;     // ceil(rows / (16 * waves))
+  int32_t row_waves;      // 1, 2, 4 (each with 2 key halves), 8 or 16: 16 rows each
+  int32_t row_groups;     // ceil(rows / (16 * row_waves))
   int32_t n_split;        // key splits per (batch, kv head, row group)
   int32_t tiles_per_split;
   int64_t cap;

@@ -134,9 +134,12 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
-// Workgroup = NW wavefronts over 16 NW packed rows (row = token * G + head in
-// group) of one KV head and one key split (16 rows per wavefront on
-// v_mfma_f32_16x16x32_bf16, see Flash16).  Each 64-key tile is staged by
+// Workgroup = RWW x KSPL wavefronts over 16 RWW packed rows (row = token * G +
+// head in group) of one KV head and one key split: 16 rows per wavefront on
+// v_mfma_f32_16x16x32_bf16 (see Flash16), and with KSPL = 2 the two halves of
+// every 64-key tile go to two wavefronts with their own softmax state, merged
+// through LDS at the end (twice the wavefronts per SIMD to hide the latency
+// of one tile's dependent MFMA / shuffle / LDS chain).  Each tile is staged by
 // direct global->LDS loads through a ring of 4 stages, three tiles ahead:
 // per tile, 64 threads first resolve every row's source (segment lookup in
 // LDS: pool block, rotated on load, or the row's own context buffer) into a
@@ -144,9 +147,10 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // rows that come from the pool in LDS, at their gathered position, before
 // the tile is used.  Lane layout and softmax: see Flash.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool FUSED>
-__global__ __launch_bounds__(64 * NW) void k_query_bf16(QueryArgs a) {
+template <int D, int RWW, int KSPL, bool FUSED>
+__global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
+  constexpr int NW = RWW * KSPL, KH = kKeyTile / KSPL;
   constexpr int KS = D / 32, OT = D / 16, CP = D / 16, CR = D / 8;
   constexpr int RW = 16;  // rows per wavefront
   constexpr int NST = 4;
@@ -159,11 +163,12 @@ __global__ __launch_bounds__(64 * NW) void k_query_bf16(QueryArgs a) {
   __shared__ uint8_t row_rot[NST][kKeyTile];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rw = wave % RWW, kh = wave / RWW;  // row wavefront, key half
   const int q16 = (lane >> 4) & 3, r16 = lane & 15;
   const int split = blockIdx.x;
   const int g = blockIdx.y % a.hkv, rg = blockIdx.y / a.hkv, b = blockIdx.z;
   const int G = a.hq / a.hkv;
-  const int wrow0 = rg * (RW * NW) + wave * RW;
+  const int wrow0 = rg * (RW * RWW) + rw * RW;
   const bool wave_live = wrow0 < a.rows;
   const int rho = wrow0 + r16;
   const bool live = rho < a.rows;
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(64 * NW) void k_query_bf16(QueryArgs a) {
   Flash16<D> fl;
   fl.init();
   int koff[KS], vbase[OT];
-  lane_offsets16<D>(lane, koff, vbase);
+  lane_offsets16<D>(lane, kh * KH, koff, vbase);
   // The in-LDS rotation handles chunk pair tid % CP of its rows: its 8
   // frequencies live in registers (no per-lane kernel-argument loads in the
   // loop, whose vector-memory counter is reserved for the tile loads).
@@ -292,13 +297,45 @@ __global__ __launch_bounds__(64 * NW) void k_query_bf16(QueryArgs a) {
       barrier_nofence();
     }
     if (wave_live) {
-      const int lim = qpos - u0;  // keys kr <= lim are visible (causal over new tokens)
-      fl.tile(st, koff, vbase, qb, u0 + kKeyTile - 1 > pos0, [=](int kr) { return kr <= lim; });
+      const int k0 = u0 + kh * KH;
+      const int lim = qpos - k0;  // keys kr <= lim are visible (causal over new tokens)
+      fl.template tile<KH>(st, koff, vbase, qb, k0 + KH - 1 > pos0,
+                           [=](int kr) { return kr <= lim; });
     }
   }
   (void)CR;
 
-  const float lsum = fl.total();
+  float lsum = fl.total();
+  if constexpr (KSPL == 2) {
+    // Second key half -> LDS (the ring is free once every wavefront is past
+    // its last tile); the first half merges: weights 2^(m_h - M) over halves
+    // that saw a key.
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(lds) + rw * (OT * 256 + 32);
+    if (kh == 1) {
+#pragma unroll
+      for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4*>(xo + (t * 64 + lane) * 4) = fl.o[t];
+      if (q16 == 0) {
+        xo[OT * 256 + 2 * r16] = fl.m;
+        xo[OT * 256 + 2 * r16 + 1] = lsum;
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xo[OT * 256 + 2 * r16], l1 = xo[OT * 256 + 2 * r16 + 1];
+    const bool h0 = lsum > 0.0f, h1 = l1 > 0.0f;
+    const float M = h0 && h1 ? fmaxf(fl.m, m1) : h1 ? m1 : fl.m;
+    const float w0 = h0 ? __builtin_amdgcn_exp2f(fl.m - M) : 0.0f;
+    const float w1 = h1 ? __builtin_amdgcn_exp2f(m1 - M) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) {
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + (t * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fl.o[t][i] = w0 * fl.o[t][i] + w1 * o1[i];
+    }
+    fl.m = M;
+    lsum = w0 * lsum + w1 * l1;
+  }
   if (!live) return;
   if (a.n_split == 1) {
     const float inv = 1.0f / lsum;
@@ -473,24 +510,26 @@ hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
   return hipGetLastError();
 }
 
-template <int D, int NW>
-static void launch_query_nw(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
-  if constexpr (D == 128 && NW == 16) {
+template <int D, int RWW, int KSPL>
+static void launch_query_w(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
+  const dim3 block(64 * RWW * KSPL);
+  if constexpr (D == 128 && RWW == 16) {
     // The host plans at most 8 wavefronts for the fused form at head_dim 128.
-    hipLaunchKernelGGL((k_query_bf16<D, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, false>), grid, block, 0, stream, a);
   } else {
-    if (fused) hipLaunchKernelGGL((k_query_bf16<D, NW, true>), grid, dim3(64 * NW), 0, stream, a);
-    else hipLaunchKernelGGL((k_query_bf16<D, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+    if (fused) hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, false>), grid, block, 0, stream, a);
   }
 }
 
 template <int D>
 static void launch_query_d(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
-  switch (a.waves) {
-    case 2: launch_query_nw<D, 2>(a, grid, fused, stream); break;
-    case 4: launch_query_nw<D, 4>(a, grid, fused, stream); break;
-    case 8: launch_query_nw<D, 8>(a, grid, fused, stream); break;
-    default: launch_query_nw<D, 16>(a, grid, fused, stream); break;
+  switch (a.row_waves) {
+    case 1: launch_query_w<D, 1, 2>(a, grid, fused, stream); break;
+    case 2: launch_query_w<D, 2, 2>(a, grid, fused, stream); break;
+    case 4: launch_query_w<D, 4, 2>(a, grid, fused, stream); break;
+    case 8: launch_query_w<D, 8, 1>(a, grid, fused, stream); break;
+    default: launch_query_w<D, 16, 1>(a, grid, fused, stream); break;
   }
 }
 
@@ -503,7 +542,7 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     return hipGetLastError();
   }
   const bool fused = a.k_pool != nullptr;
-  if (fused && head_dim == 128 && a.waves > 8) return hipErrorInvalidValue;
+  if (fused && head_dim == 128 && a.row_waves > 8) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
   if (head_dim == 128) launch_query_d<128>(a, grid, fused, stream);
   else launch_query_d<64>(a, grid, fused, stream);

@@ -256,6 +256,12 @@ def test_anchor_only_and_single_token():
     _stage2_case("bf16", 4, 4, 128, lens, np.array([[0]], np.int32), 1, 1e4, 131, False)
     _stage2_case("bf16", 4, 4, 128, lens, np.array([[0]], np.int32), 1, 1e4, 131, True)
     _stage2_case("bf16", 4, 1, 64, lens, np.array([[0, 2]], np.int32), 3, 1e4, 141, True)
+    # Context of 21 keys: the wavefronts holding keys 32..63 of the only tile
+    # see none, and their (empty) softmax state must carry zero weight.
+    short = np.array([20, 9], np.int32)
+    for fused in (False, True):
+        _stage2_case("bf16", 4, 4, 128, short, np.array([[0]], np.int32), 1, 1e4, 143, fused)
+        _stage2_case("bf16", 8, 2, 64, short, np.array([[0, 1]], np.int32), 2, 1e4, 145, fused)
 
 
 @pytest.mark.parametrize("fused", [False, True])
