@@ -278,16 +278,14 @@ struct QueryPlan {
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
-void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max_ctx, bool fused,
+void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max_ctx,
                  QueryPlan& qp) {
   const int G = a->n_q_heads / a->n_kv_heads;
   qp.rows = n_new * G;
   // 16 packed rows per row wavefront; up to 4 of them split every key tile
-  // between two wavefronts (so 2 .. 8 wavefronts), 8 or 16 take whole tiles.
-  // The fused gather keeps RoPE frequencies in registers and would spill at
-  // 16 wavefronts (128 VGPRs each) for head_dim 128, so it stops at 8.
-  qp.row_waves = qp.rows <= 16 ? 1 : qp.rows <= 32 ? 2 : qp.rows <= 64 ? 4 : qp.rows <= 128 ? 8 : 16;
-  if (fused && a->head_dim == 128) qp.row_waves = std::min(qp.row_waves, 8);
+  // between two wavefronts (so 2 .. 8 wavefronts), 8 take whole tiles; more
+  // rows use more row groups.
+  qp.row_waves = qp.rows <= 16 ? 1 : qp.rows <= 32 ? 2 : qp.rows <= 64 ? 4 : 8;
   qp.row_groups = (int32_t)cdiv(qp.rows, 16 * qp.row_waves);
   const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
   qp.n_split = 1;
@@ -338,24 +336,32 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
                       const void* v_pool, void* k_buf, void* v_buf, int64_t cap, void* o,
                       const SegPlan& sp, const QueryPlan& qp, void* ws, hipStream_t s) {
   char* w = static_cast<char*>(ws);
-  int rc = stage_bytes(sp.tables.data(), qp.meta_bytes, w + qp.off_meta, s);
-  if (rc) return rc;
+  const bool bf16 = a->dtype == DBSA_BF16;
+  // bf16: small tables ride in the kernel arguments (no copy, no extra
+  // queue operation); otherwise they are staged into the workspace.
+  const bool inl = bf16 && sp.tables.size() <= (size_t)kInlineInts;
   const int32_t* dt = reinterpret_cast<const int32_t*>(w + qp.off_meta);
+  if (!inl) {
+    const int rc = stage_bytes(sp.tables.data(), qp.meta_bytes, w + qp.off_meta, s);
+    if (rc) return rc;
+  }
   const RopeFreq freq = make_freq(a);
-
-  NewKVArgs na;
-  na.k_new = k_new;
-  na.v_new = v_new;
-  na.k_dst = k_buf;
-  na.v_dst = v_buf;
-  na.dst_row = dt + sp.o_dst;
-  na.pos0 = dt + sp.o_pos0;
-  na.n_new = n_new;
-  na.hkv = a->n_kv_heads;
-  na.cap = cap;
-  na.freq = freq;
-  hipError_t e = launch_new_kv(na, batch, a->head_dim, a->dtype, s);
-  if (e != hipSuccess) return hip_fail(e, "launch new_kv");
+  hipError_t e;
+  if (!bf16) {
+    NewKVArgs na;
+    na.k_new = k_new;
+    na.v_new = v_new;
+    na.k_dst = k_buf;
+    na.v_dst = v_buf;
+    na.dst_row = dt + sp.o_dst;
+    na.pos0 = dt + sp.o_pos0;
+    na.n_new = n_new;
+    na.hkv = a->n_kv_heads;
+    na.cap = cap;
+    na.freq = freq;
+    e = launch_new_kv(na, batch, a->head_dim, a->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "launch new_kv");
+  }
 
   QueryArgs qa;
   qa.q = q;
@@ -363,15 +369,21 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.v_pool = v_pool;
   qa.k_ctx = k_buf;
   qa.v_ctx = v_buf;
+  qa.k_new = k_new;
+  qa.v_new = v_new;
   qa.o = o;
   qa.part_o = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_po) : nullptr;
   qa.part_ml = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_ml) : nullptr;
-  qa.seg.start = dt + sp.o_start;
-  qa.seg.src = dt + sp.o_src;
-  qa.seg.buf = dt + sp.o_buf;
-  qa.seg.nseg = dt + sp.o_nseg;
-  qa.seg.seg_stride = sp.stride;
-  qa.pos0 = dt + sp.o_pos0;
+  qa.meta = inl ? nullptr : dt;
+  qa.seg.o_start = (int32_t)sp.o_start;
+  qa.seg.o_src = (int32_t)sp.o_src;
+  qa.seg.o_buf = (int32_t)sp.o_buf;
+  qa.seg.o_nseg = (int32_t)sp.o_nseg;
+  qa.seg.o_pos0 = (int32_t)sp.o_pos0;
+  qa.seg.o_dst = (int32_t)sp.o_dst;
+  qa.seg.stride = sp.stride;
+  qa.n_inline = inl ? (int32_t)sp.tables.size() : 0;
+  if (inl) std::memcpy(qa.inl, sp.tables.data(), sp.tables.size() * sizeof(int32_t));
   qa.n_new = n_new;
   qa.hq = a->n_q_heads;
   qa.hkv = a->n_kv_heads;
@@ -527,9 +539,9 @@ size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t
         fail(DBSA_EINVAL, "n_ids must be >= 1");
         return 0;
       }
-      const int32_t stride = op == DBSA_OP_QUERY ? 2 : n_ids + 2;
+      const int32_t stride = op == DBSA_OP_QUERY ? 3 : n_ids + 3;
       QueryPlan qp;
-      query_split(attn, batch, (int32_t)rows, max_ctx, op == DBSA_OP_QUERY_GATHERED, qp);
+      query_split(attn, batch, (int32_t)rows, max_ctx, qp);
       query_layout(attn, batch, seg_meta_ints(batch, stride), qp);
       if (check_meta(qp.meta_bytes)) return 0;
       return qp.total;
@@ -643,22 +655,36 @@ int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const
   }
   if (max_ctx >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
   QueryPlan qp;
-  query_split(attn, batch, n_new, max_ctx, false, qp);
+  query_split(attn, batch, n_new, max_ctx, qp);
   SegPlan sp;
-  seg_init(sp, batch, 2);
+  seg_init(sp, batch, 3);
   query_layout(attn, batch, sp.tables.size(), qp);
   rc = check_meta(qp.meta_bytes);
   if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
   if (rc) return rc;
+  // bf16: context buffer rows [0, ctx_len), then the new tokens read from
+  // k_new / v_new.  float32: the new tokens are appended first (new_kv) and
+  // the whole range is read from the context buffer.
+  const bool bf16 = attn->dtype == DBSA_BF16;
   for (int b = 0; b < batch; ++b) {
-    int32_t* t = sp.tables.data();
-    t[sp.o_start + (size_t)b * 2 + 0] = 0;
-    t[sp.o_start + (size_t)b * 2 + 1] = (int32_t)(ctx_len[b] + n_new);
-    t[sp.o_src + (size_t)b * 2] = 0;
-    t[sp.o_buf + (size_t)b * 2] = 1;
-    t[sp.o_nseg + b] = 1;
-    t[sp.o_pos0 + b] = (int32_t)ctx_len[b];
-    t[sp.o_dst + b] = (int32_t)ctx_len[b];
+    int32_t* t = sp.tables.data() + 0;
+    const size_t r3 = (size_t)b * 3;
+    const int32_t cl = (int32_t)ctx_len[b];
+    t[sp.o_start + r3 + 0] = 0;
+    t[sp.o_src + r3 + 0] = 0;
+    t[sp.o_buf + r3 + 0] = 1;
+    if (bf16) {
+      t[sp.o_start + r3 + 1] = cl;
+      t[sp.o_src + r3 + 1] = 0;
+      t[sp.o_buf + r3 + 1] = 2;
+      t[sp.o_start + r3 + 2] = cl + n_new;
+      t[sp.o_nseg + b] = 2;
+    } else {
+      t[sp.o_start + r3 + 1] = cl + n_new;
+      t[sp.o_nseg + b] = 1;
+    }
+    t[sp.o_pos0 + b] = cl;
+    t[sp.o_dst + b] = cl;
   }
   return launch_query_path(attn, batch, n_new, q, k_new, v_new, nullptr, nullptr, k_ctx, v_ctx,
                            ctx_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
@@ -684,10 +710,14 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
   rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
                   "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
   if (rc) return rc;
-  if (n_ids + 1 > kMaxSegments)
+  if (n_ids + 2 > kMaxSegments)
     return fail(DBSA_EUNSUPPORTED, "n_ids %d exceeds the %d supported blocks per query", n_ids,
-                kMaxSegments - 1);
-  const int32_t stride = n_ids + 2;
+                kMaxSegments - 2);
+  // Segments: the selected pool blocks (rotated on load), then the row's tail
+  // buffer, then (bf16) the new tokens read from k_new / v_new; float32
+  // appends the new tokens to the tail buffer first and reads them there.
+  const bool bf16 = attn->dtype == DBSA_BF16;
+  const int32_t stride = n_ids + 3;
   SegPlan sp;
   seg_init(sp, batch, stride);
   int64_t max_ctx = 0;
@@ -697,27 +727,36 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
       return fail(DBSA_ENOSPC, "tail_len[%d] + n_new = %lld exceeds tail_capacity %lld", b,
                   (long long)(tail_len[b] + n_new), (long long)tail_capacity);
     int32_t* t = sp.tables.data();
+    const size_t row = (size_t)b * stride;
     int64_t pos = 0;
     for (int i = 0; i < n_ids; ++i) {
       const int blkid = ids[(int64_t)b * n_ids + i];
-      t[sp.o_start + (size_t)b * stride + i] = (int32_t)pos;
-      t[sp.o_src + (size_t)b * stride + i] = off[blkid];
-      t[sp.o_buf + (size_t)b * stride + i] = 0;
+      t[sp.o_start + row + i] = (int32_t)pos;
+      t[sp.o_src + row + i] = off[blkid];
+      t[sp.o_buf + row + i] = 0;
       pos += off[blkid + 1] - off[blkid];
     }
     const int64_t total = pos + tail_len[b] + n_new;
     if (total >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
-    t[sp.o_start + (size_t)b * stride + n_ids] = (int32_t)pos;  // tail segment
-    t[sp.o_src + (size_t)b * stride + n_ids] = 0;
-    t[sp.o_buf + (size_t)b * stride + n_ids] = 1;
-    t[sp.o_start + (size_t)b * stride + n_ids + 1] = (int32_t)total;
-    t[sp.o_nseg + b] = n_ids + 1;
+    t[sp.o_start + row + n_ids] = (int32_t)pos;  // tail segment
+    t[sp.o_src + row + n_ids] = 0;
+    t[sp.o_buf + row + n_ids] = 1;
+    if (bf16) {
+      t[sp.o_start + row + n_ids + 1] = (int32_t)(pos + tail_len[b]);  // new tokens
+      t[sp.o_src + row + n_ids + 1] = 0;
+      t[sp.o_buf + row + n_ids + 1] = 2;
+      t[sp.o_start + row + n_ids + 2] = (int32_t)total;
+      t[sp.o_nseg + b] = n_ids + 2;
+    } else {
+      t[sp.o_start + row + n_ids + 1] = (int32_t)total;
+      t[sp.o_nseg + b] = n_ids + 1;
+    }
     t[sp.o_pos0 + b] = (int32_t)(pos + tail_len[b]);
     t[sp.o_dst + b] = (int32_t)tail_len[b];
     max_ctx = std::max(max_ctx, total);
   }
   QueryPlan qp;
-  query_split(attn, batch, n_new, max_ctx, true, qp);
+  query_split(attn, batch, n_new, max_ctx, qp);
   query_layout(attn, batch, sp.tables.size(), qp);
   rc = check_meta(qp.meta_bytes);
   if (!rc) rc = check_ws(ws, ws_bytes, qp.total);

@@ -67,14 +67,23 @@ struct PrefillArgs {
 // ---------------------------------------------------------------------------
 // The context of batch row b is a list of segments of virtual positions.
 // Segment s covers positions [start[s], start[s+1]); its tokens are read from
-// `src` token index onward in buffer `buf` (0 = unrotated pool, rotated on
-// load at the virtual position; 1 = the row's own rotated context buffer).
+// `src` token index onward in buffer `buf`:
+//   0  the unrotated pool (rotated on load at the virtual position),
+//   1  the row's own rotated context buffer,
+//   2  the call's new tokens (rotated on load; written back, rotated, to the
+//      context buffer at dst_row + token).
+// The tables are int32 arrays at these offsets of one table block, which
+// travels in the kernel arguments when it fits (kInlineInts) and otherwise in
+// the workspace.
+constexpr int kInlineInts = 512;
 struct SegTable {
-  const int32_t* start;   // [batch][seg_stride]  (start[nseg] = context length)
-  const int32_t* src;     // [batch][seg_stride]
-  const int32_t* buf;     // [batch][seg_stride]
-  const int32_t* nseg;    // [batch]
-  int32_t seg_stride;
+  int32_t o_start;   // [batch][stride]  (start[nseg] = context length)
+  int32_t o_src;     // [batch][stride]
+  int32_t o_buf;     // [batch][stride]
+  int32_t o_nseg;    // [batch]
+  int32_t o_pos0;    // [batch] position of new token 0 (= keys before it)
+  int32_t o_dst;     // [batch] context-buffer row of new token 0
+  int32_t stride;
 };
 
 struct GatherArgs {
@@ -106,22 +115,26 @@ struct QueryArgs {
   const void* q;          // [batch][n_new][hq][d]
   const void* k_pool;     // may be null when no segment uses buffer 0
   const void* v_pool;
-  const void* k_ctx;      // [batch][cap][hkv][d]
-  const void* v_ctx;
+  void* k_ctx;            // [batch][cap][hkv][d] (buffer 1; new rows are written here)
+  void* v_ctx;
+  const void* k_new;      // [batch][n_new][hkv][d] (buffer 2)
+  const void* v_new;
   void* o;                // [batch][n_new][hq][d] (when n_split == 1)
   float* part_o;          // [batch][hkv][n_split][rows][d] (when n_split > 1)
   float* part_ml;         // [batch][hkv][n_split][rows][2]
+  const int32_t* meta;    // table block in device memory (when n_inline == 0)
   SegTable seg;
-  const int32_t* pos0;    // [batch] position of new token 0 (= keys before it)
+  int32_t n_inline;       // > 0: the table block is `inl` below
   int32_t n_new, hq, hkv;
   int32_t rows;           // n_new * (hq / hkv) packed rows per kv head
-  int32_t row_waves;      // 1, 2, 4 (each with 2 key halves), 8 or 16: 16 rows each
+  int32_t row_waves;      // 1, 2, 4 (each with 2 key halves) or 8: 16 rows each
   int32_t row_groups;     // ceil(rows / (16 * row_waves))
   int32_t n_split;        // key splits per (batch, kv head, row group)
   int32_t tiles_per_split;
   int64_t cap;
   float q_scale;          // softmax scale * log2(e)
   RopeFreq freq;
+  int32_t inl[kInlineInts];
 };
 
 struct CombineArgs {

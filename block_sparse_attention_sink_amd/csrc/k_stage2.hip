@@ -8,12 +8,14 @@
 // Kernels
 //   k_gather_bf16 / k_gather_f32   materialise the gathered, re-rotated K and
 //                                  the gathered V (HBM-bound copy + rotate).
-//   k_new_kv_bf16 / k_new_kv_f32   rotate the new tokens' K at their positions
-//                                  and append K/V to the row's context buffer.
-//   k_query_bf16<D, FUSED>         split-K flash attention of the packed
+//   k_new_kv_f32                   rotate the new tokens' K at their positions
+//                                  and append K/V to the row's context buffer
+//                                  (float32 path; bf16 does it in k_query_bf16).
+//   k_query_bf16<D, RWW, KSPL>     split-K flash attention of the packed
 //                                  (token, head-in-group) rows of one KV head
-//                                  over a segment list; FUSED reads pool blocks
-//                                  directly and rotates K while staging it.
+//                                  over a segment list (pool blocks and new
+//                                  tokens are rotated while staged; new tokens
+//                                  are also appended to the context buffer).
 //   k_combine                      log-sum-exp merge of the split partials.
 //   k_query_f32                    float32 rows (one wavefront per row).
 #include "dbsa_device.hpp"
@@ -85,29 +87,6 @@ __global__ __launch_bounds__(256) void k_gather_f32(GatherArgs a) {
 // New tokens: rotate K at its position, append K/V to the context buffer.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_new_kv_bf16(NewKVArgs a) {
-  constexpr int CP = D / 16, CR = D / 8;
-  const int r = blockIdx.x, b = blockIdx.y;
-  const int64_t pos = (int64_t)a.pos0[b] + r;
-  const int64_t row = (int64_t)a.dst_row[b] + r;
-  for (int u = threadIdx.x; u < a.hkv * CP; u += blockDim.x) {
-    const int g = u / CP, c = u % CP;
-    const int64_t src = ((((int64_t)b * a.n_new + r) * a.hkv) + g) * CR;
-    const int64_t dst = (((int64_t)b * a.cap + row) * a.hkv + g) * CR;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_new);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_new);
-    u32x4 k1 = kp[src + c], k2 = kp[src + c + CP];
-    rope_rotate_chunk(k1, k2, pos, a.freq, 8 * c);
-    u32x4* ko = reinterpret_cast<u32x4*>(a.k_dst);
-    u32x4* vo = reinterpret_cast<u32x4*>(a.v_dst);
-    ko[dst + c] = k1;
-    ko[dst + c + CP] = k2;
-    vo[dst + c] = vp[src + c];
-    vo[dst + c + CP] = vp[src + c + CP];
-  }
-}
-
-template <int D>
 __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
   constexpr int H = D / 2;
   const int r = blockIdx.x, b = blockIdx.y;
@@ -132,6 +111,17 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Segment tables: in the kernel arguments (read through the kernarg segment
+// pointer, so no private copy is made) or in device memory.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
+  if (a.n_inline)
+    return reinterpret_cast<const int32_t*>((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                            offsetof(QueryArgs, inl));
+  return a.meta;
+}
+
+// ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
 // Workgroup = RWW x KSPL wavefronts over 16 RWW packed rows (row = token * G +
@@ -141,13 +131,14 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // through LDS at the end (twice the wavefronts per SIMD to hide the latency
 // of one tile's dependent MFMA / shuffle / LDS chain).  Each tile is staged by
 // direct global->LDS loads through a ring of 4 stages, three tiles ahead:
-// per tile, 64 threads first resolve every row's source (segment lookup in
-// LDS: pool block, rotated on load, or the row's own context buffer) into a
-// small address table, then all waves issue the loads.  FUSED rotates the K
-// rows that come from the pool in LDS, at their gathered position, before
-// the tile is used.  Lane layout and softmax: see Flash.
+// per tile, wavefront 0 first resolves every row's source (segment lookup in
+// LDS) into a small address table, then all wavefronts issue the loads.
+// Rows from the pool or from the new tokens arrive unrotated and are rotated
+// in LDS at their virtual position before the tile is used; the first row
+// group also writes the new tokens' rotated K and their V to the context
+// buffer (each new token lies in exactly one tile of one split).
 // ---------------------------------------------------------------------------
-template <int D, int RWW, int KSPL, bool FUSED>
+template <int D, int RWW, int KSPL>
 __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
   constexpr int NW = RWW * KSPL, KH = kKeyTile / KSPL;
@@ -157,10 +148,14 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   constexpr int INSTR = Gm::TU4 / 64;  // 1 KiB loads per matrix per tile
   constexpr int LPW = 2 * INSTR / NW;  // loads per wave per tile
   static_assert((2 * INSTR) % NW == 0, "loads must split evenly over the waves");
+  static_assert((64 * NW) % CP == 0, "each thread keeps one chunk pair");
+  constexpr uint8_t kRot = 1, kNew = 2;
   __shared__ __align__(16) char lds[NST * Gm::STAGE];
   __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
   __shared__ uint64_t row_k[NST][kKeyTile], row_v[NST][kKeyTile];
-  __shared__ uint8_t row_rot[NST][kKeyTile];
+  __shared__ int32_t row_dst[NST][kKeyTile];
+  __shared__ uint8_t row_flag[NST][kKeyTile];
+  __shared__ uint8_t tile_flag[2 * NST];  // indexed by tile % 8 (see plan)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rw = wave % RWW, kh = wave / RWW;  // row wavefront, key half
@@ -174,15 +169,22 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   const bool live = rho < a.rows;
   const int r = live ? rho / G : 0;
   const int head = g * G + (live ? rho - (rho / G) * G : 0);
-  const int pos0 = a.pos0[b];
+  const int32_t* tab = seg_block(a);
+  const int pos0 = tab[a.seg.o_pos0 + b];
+  const int dst0 = tab[a.seg.o_dst + b];
   const int qpos = pos0 + r;
 
-  const int nseg = a.seg.nseg[b];
-  for (int i = tid; i <= nseg; i += 64 * NW) {
-    seg_start[i] = a.seg.start[(int64_t)b * a.seg.seg_stride + i];
-    if (i < nseg) {
-      seg_src[i] = a.seg.src[(int64_t)b * a.seg.seg_stride + i];
-      seg_buf[i] = a.seg.buf[(int64_t)b * a.seg.seg_stride + i];
+  const int nseg = tab[a.seg.o_nseg + b];
+  {
+    const int32_t* st = tab + a.seg.o_start + b * a.seg.stride;
+    const int32_t* sr = tab + a.seg.o_src + b * a.seg.stride;
+    const int32_t* sb = tab + a.seg.o_buf + b * a.seg.stride;
+    for (int i = tid; i <= nseg; i += 64 * NW) {
+      seg_start[i] = st[i];
+      if (i < nseg) {
+        seg_src[i] = sr[i];
+        seg_buf[i] = sb[i];
+      }
     }
   }
 
@@ -206,28 +208,38 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   const int it0 = split * a.tiles_per_split;
   const int cnt = max(0, min(it0 + a.tiles_per_split, n_tiles) - it0);
 
-  const uint64_t kpool_u = reinterpret_cast<uint64_t>(a.k_pool);
-  const uint64_t vpool_u = reinterpret_cast<uint64_t>(a.v_pool);
-  const uint64_t kctx_u = reinterpret_cast<uint64_t>(a.k_ctx);
-  const uint64_t vctx_u = reinterpret_cast<uint64_t>(a.v_ctx);
+  // Per-source base addresses (bf16 elements -> bytes) and row strides.
+  const uint64_t kb0 = reinterpret_cast<uint64_t>(a.k_pool), vb0 = reinterpret_cast<uint64_t>(a.v_pool);
+  const uint64_t kb1 = reinterpret_cast<uint64_t>(a.k_ctx), vb1 = reinterpret_cast<uint64_t>(a.v_ctx);
+  const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
+  const int64_t tok0_1 = (int64_t)b * a.cap, tok0_2 = (int64_t)b * a.n_new;
 
-  // Row sources of local tile li (threads 0..63, one row each).
+  // Row sources of local tile li (wavefront 0, one row per lane).  The tile
+  // flags are double-buffered over 8 tiles: a slow wavefront may still read
+  // tile li-1's flag while tile li+3's is being written.
   auto plan = [&](int li) {
-    if (tid < kKeyTile) {
-      const int u_real = (it0 + li) * kKeyTile + tid;
+    if (wave == 0) {
+      const int u_real = (it0 + li) * kKeyTile + lane;
+      const bool real = u_real < T;
       const int u = min(u_real, T - 1);  // rows past the context repeat the last row (masked)
       const int s = upper_index(seg_start, nseg, u);
       const int64_t tok = seg_src[s] + (u - seg_start[s]);
-      const bool pool = FUSED && seg_buf[s] == 0;
-      // Branch-free select of the source tensor (a pointer select here is
-      // otherwise lowered to a lookup table in scratch memory).
-      const uint64_t m = pool ? ~0ull : 0ull;
-      const uint64_t off =
-          2ull * static_cast<uint64_t>(((pool ? 0 : (int64_t)b * a.cap) + tok) * a.hkv + g) * D;
+      const int buf = seg_buf[s];
+      // Branch-free select of the source (a pointer select here is otherwise
+      // lowered to a lookup table in scratch memory).
+      const uint64_t m0 = buf == 0 ? ~0ull : 0ull, m1 = buf == 1 ? ~0ull : 0ull;
+      const uint64_t m2 = ~(m0 | m1);
+      const int64_t trow = (buf == 0 ? 0 : buf == 1 ? tok0_1 : tok0_2) + tok;
+      const uint64_t off = 2ull * static_cast<uint64_t>((trow * a.hkv + g) * D);
       const int slot = li % NST;
-      row_k[slot][tid] = ((kpool_u & m) | (kctx_u & ~m)) + off;
-      row_v[slot][tid] = ((vpool_u & m) | (vctx_u & ~m)) + off;
-      row_rot[slot][tid] = pool && u_real < T;
+      row_k[slot][lane] = ((kb0 & m0) | (kb1 & m1) | (kb2 & m2)) + off;
+      row_v[slot][lane] = ((vb0 & m0) | (vb1 & m1) | (vb2 & m2)) + off;
+      const uint8_t f = real ? (buf != 1 ? kRot : 0) | (buf == 2 ? kNew : 0) : 0;
+      row_flag[slot][lane] = f;
+      row_dst[slot][lane] = dst0 + (int)tok;
+      const uint64_t any_rot = __builtin_amdgcn_ballot_w64(f & kRot);
+      const uint64_t any_new = __builtin_amdgcn_ballot_w64(f & kNew);
+      if (lane == 0) tile_flag[li & (2 * NST - 1)] = (any_rot ? kRot : 0) | (any_new ? kNew : 0);
     }
   };
   // Loads of local tile li into its stage (all waves).
@@ -262,10 +274,9 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   // frequencies live in registers (no per-lane kernel-argument loads in the
   // loop, whose vector-memory counter is reserved for the tile loads).
   double fr[8];
-  if constexpr (FUSED) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (tid % CP) + i];
-  }
+  for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (tid % CP) + i];
+  const bool writer = rg == 0;  // one row group writes the new tokens back
 
   for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
   waitcnt<0, 0>();
@@ -278,20 +289,33 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
     wait_vm<true>(LPW * min(NST - 2, cnt - 1 - li));
     barrier_nofence();
     if (li + NST - 1 < cnt) load(li + NST - 1);
-    char* st = lds + (li % NST) * Gm::STAGE;
+    const int slot = li % NST;
+    char* st = lds + slot * Gm::STAGE;
     const int u0 = (it0 + li) * kKeyTile;
-    if constexpr (FUSED) {
-      // Re-apply RoPE at the gathered position to the K rows from the pool.
-      static_assert((64 * NW) % CP == 0, "each thread keeps one chunk pair");
+    const uint8_t tf = tile_flag[li & (2 * NST - 1)];
+    if (tf & kRot) {
+      // RoPE at the virtual position for pool rows and new tokens; the new
+      // tokens' rotated K (from registers) and V go to the context buffer.
       for (int uidx = tid; uidx < kKeyTile * CP; uidx += 64 * NW) {
         const int row = uidx / CP, c = uidx - row * CP;
-        if (!row_rot[li % NST][row]) continue;
+        const uint8_t f = row_flag[slot][row];
+        if (!(f & kRot)) continue;
         u32x4* k1 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c) * 16);
         u32x4* k2 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c + CP) * 16);
         u32x4 x1 = *k1, x2 = *k2;
         rope_rotate_chunk_f(x1, x2, u0 + row, fr);
         *k1 = x1;
         *k2 = x2;
+        if ((f & kNew) && writer) {
+          const int64_t d = (((int64_t)b * a.cap + row_dst[slot][row]) * a.hkv + g) * CR;
+          u32x4* ko = static_cast<u32x4*>(a.k_ctx);
+          u32x4* vo = static_cast<u32x4*>(a.v_ctx);
+          const char* vs = st + Gm::KBYTES + row * Gm::ROW;
+          ko[d + c] = x1;
+          ko[d + c + CP] = x2;
+          vo[d + c] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c) * 16);
+          vo[d + c + CP] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c + CP) * 16);
+        }
       }
       waitcnt<63, 0>();
       barrier_nofence();
@@ -360,32 +384,57 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over
+// the splits that saw a key (l_s > 0).  One thread per 4 head dims; the
+// partials of 8 splits are loaded at once and merged online batch by batch.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(D) void k_combine(CombineArgs a) {
-  const int rho = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR, SB = 8;
+  const int rho = blockIdx.x * RPB + threadIdx.x / TPR, d4 = threadIdx.x % TPR;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (rho >= a.rows) return;
   const int G = a.hq / a.hkv;
   const int r = rho / G, head = g * G + rho % G;
   const int64_t base = ((int64_t)b * a.hkv + g) * a.n_split;
-  // Reference = largest split reference among splits that saw a key; splits
-  // with no keys (l = 0) contribute nothing.
-  float M = kNegInf;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t prow = (base + s) * a.rows + rho;
-    if (a.part_ml[prow * 2 + 1] > 0.0f) M = fmaxf(M, a.part_ml[prow * 2]);
+  float M = kNegInf, L = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < a.n_split; s0 += SB) {
+    float m[SB], l[SB];
+    f32x4 o[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const bool in = s0 + i < a.n_split;
+      const int64_t prow = (base + s0 + i) * a.rows + rho;
+      // (m, l) as one float pair.  (__builtin_bit_cast of a vector element
+      // compiles to element 0 here, so no bit casts of lanes.)
+      const f32x2 ml = in ? *reinterpret_cast<const f32x2*>(a.part_ml + prow * 2) : f32x2{0.0f, 0.0f};
+      m[i] = ml[0];
+      l[i] = ml[1];
+      o[i] = in ? *reinterpret_cast<const f32x4*>(a.part_o + prow * D + 4 * d4) : f32x4{};
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) Mb = l[i] > 0.0f ? fmaxf(Mb, m[i]) : Mb;
+    const float sc = L > 0.0f ? __builtin_amdgcn_exp2f(M - Mb) : 0.0f;
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const float w = l[i] > 0.0f ? __builtin_amdgcn_exp2f(m[i] - Mb) : 0.0f;
+      L += w * l[i];
+      acc += w * o[i];
+    }
+    M = Mb;
   }
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t prow = (base + s) * a.rows + rho;
-    if (!(a.part_ml[prow * 2 + 1] > 0.0f)) continue;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
-    L += w * a.part_ml[prow * 2 + 1];
-    acc += w * a.part_o[prow * D + d];
+  const float inv = 1.0f / L;
+  const int64_t od = (((int64_t)b * a.n_new + r) * a.hq + head) * D + 4 * d4;
+  if constexpr (BF16) {
+    const u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + od) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + od) = acc * inv;
   }
-  const int64_t o = (((int64_t)b * a.n_new + r) * a.hq + head) * D + d;
-  if (BF16) static_cast<uint16_t*>(a.o)[o] = to_bf16(acc / L);
-  else static_cast<float*>(a.o)[o] = acc / L;
 }
 
 // ---------------------------------------------------------------------------
@@ -400,7 +449,8 @@ __global__ __launch_bounds__(256) void k_query_f32(QueryArgs a) {
   if (idx >= a.n_new * a.hq) return;      // no block-level synchronisation below
   const int r = idx / a.hq, head = idx % a.hq;
   const int g = head / (a.hq / a.hkv);
-  const int qpos = a.pos0[b] + r;
+  const int32_t* tab = seg_block(a);
+  const int qpos = tab[a.seg.o_pos0 + b] + r;
   const float* q = static_cast<const float*>(a.q) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
   float qr[D];
 #pragma unroll
@@ -410,10 +460,10 @@ __global__ __launch_bounds__(256) void k_query_f32(QueryArgs a) {
     qr[i] = rot_lo(q[i], q[i + H], c, s) * a.q_scale;
     qr[i + H] = rot_hi(q[i], q[i + H], c, s) * a.q_scale;
   }
-  const int nseg = a.seg.nseg[b];
-  const int32_t* sst = a.seg.start + (int64_t)b * a.seg.seg_stride;
-  const int32_t* ssrc = a.seg.src + (int64_t)b * a.seg.seg_stride;
-  const int32_t* sbuf = a.seg.buf + (int64_t)b * a.seg.seg_stride;
+  const int nseg = tab[a.seg.o_nseg + b];
+  const int32_t* sst = tab + a.seg.o_start + b * a.seg.stride;
+  const int32_t* ssrc = tab + a.seg.o_src + b * a.seg.stride;
+  const int32_t* sbuf = tab + a.seg.o_buf + b * a.seg.stride;
   const float* kpool = static_cast<const float*>(a.k_pool);
   const float* vpool = static_cast<const float*>(a.v_pool);
   const float* kctx = static_cast<const float*>(a.k_ctx);
@@ -500,36 +550,19 @@ hipError_t launch_gather(const GatherArgs& a, int batch, int head_dim, int dtype
 hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
                          hipStream_t stream) {
   const dim3 grid(a.n_new, batch);
-  if (dtype == 1) {
-    if (head_dim == 128) hipLaunchKernelGGL(k_new_kv_f32<128>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_new_kv_f32<64>, grid, dim3(256), 0, stream, a);
-  } else {
-    if (head_dim == 128) hipLaunchKernelGGL(k_new_kv_bf16<128>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_new_kv_bf16<64>, grid, dim3(256), 0, stream, a);
-  }
+  if (dtype != 1) return hipErrorInvalidValue;  // bf16 appends inside k_query_bf16
+  if (head_dim == 128) hipLaunchKernelGGL(k_new_kv_f32<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(k_new_kv_f32<64>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int RWW, int KSPL>
-static void launch_query_w(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
-  const dim3 block(64 * RWW * KSPL);
-  if constexpr (D == 128 && RWW == 16) {
-    // The host plans at most 8 wavefronts for the fused form at head_dim 128.
-    hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, false>), grid, block, 0, stream, a);
-  } else {
-    if (fused) hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_query_bf16<D, RWW, KSPL, false>), grid, block, 0, stream, a);
-  }
-}
-
 template <int D>
-static void launch_query_d(const QueryArgs& a, dim3 grid, bool fused, hipStream_t stream) {
+static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
   switch (a.row_waves) {
-    case 1: launch_query_w<D, 1, 2>(a, grid, fused, stream); break;
-    case 2: launch_query_w<D, 2, 2>(a, grid, fused, stream); break;
-    case 4: launch_query_w<D, 4, 2>(a, grid, fused, stream); break;
-    case 8: launch_query_w<D, 8, 1>(a, grid, fused, stream); break;
-    default: launch_query_w<D, 16, 1>(a, grid, fused, stream); break;
+    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(128), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(512), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_query_bf16<D, 8, 1>), grid, dim3(512), 0, stream, a); break;
   }
 }
 
@@ -541,23 +574,24 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     else hipLaunchKernelGGL(k_query_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const bool fused = a.k_pool != nullptr;
-  if (fused && head_dim == 128 && a.row_waves > 8) return hipErrorInvalidValue;
+  if (a.row_waves != 1 && a.row_waves != 2 && a.row_waves != 4 && a.row_waves != 8)
+    return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
-  if (head_dim == 128) launch_query_d<128>(a, grid, fused, stream);
-  else launch_query_d<64>(a, grid, fused, stream);
+  if (head_dim == 128) launch_query_d<128>(a, grid, stream);
+  else launch_query_d<64>(a, grid, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, int batch, int head_dim, int dtype,
                           hipStream_t stream) {
-  const dim3 grid(a.rows, a.hkv, batch);
+  const int rpb = 256 / (head_dim / 4);
+  const dim3 grid((a.rows + rpb - 1) / rpb, a.hkv, batch);
   if (head_dim == 128) {
-    if (dtype == 1) hipLaunchKernelGGL((k_combine<128, false>), grid, dim3(128), 0, stream, a);
-    else hipLaunchKernelGGL((k_combine<128, true>), grid, dim3(128), 0, stream, a);
+    if (dtype == 1) hipLaunchKernelGGL((k_combine<128, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_combine<128, true>), grid, dim3(256), 0, stream, a);
   } else {
-    if (dtype == 1) hipLaunchKernelGGL((k_combine<64, false>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((k_combine<64, true>), grid, dim3(64), 0, stream, a);
+    if (dtype == 1) hipLaunchKernelGGL((k_combine<64, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_combine<64, true>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
