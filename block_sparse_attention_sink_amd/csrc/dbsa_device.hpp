@@ -53,6 +53,18 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double rev, float& c, float
   c = __builtin_amdgcn_cosf(x);
 }
 
+// cos / sin of the sum of two angles from theirs (angle addition, explicit
+// fused multiply-adds so every kernel rounds it identically).  bf16 K rows are
+// rotated at position p = 64 t + r (t = p / 64, r = p % 64) as the sum of the
+// angles at 64 t and at r: one angle per frequency is shared by a whole 64-row
+// tile and one per row offset is fixed per thread, which replaces most of the
+// per-element sine / cosine work (about 3e-7 absolute error in c and s).
+__device__ __forceinline__ void angle_add(float ca, float sa, float cb, float sb, float& c,
+                                          float& s) {
+  c = __builtin_fmaf(ca, cb, -(sa * sb));
+  s = __builtin_fmaf(sa, cb, ca * sb);
+}
+
 // One rotate-half pair (a, b) turned by the angle with cosine c and sine s.
 // Written with explicit fused multiply-adds so that every kernel rounds the
 // rotation identically (no context-dependent contraction).
@@ -90,14 +102,6 @@ __device__ __forceinline__ void rotate_chunk(u32x4& x1, u32x4& x2, const float (
   x2 = u32x4{ob[0], ob[1], ob[2], ob[3]};
 }
 
-// Rotation of one chunk pair at `pos` with the 8 frequencies held in registers.
-__device__ __forceinline__ void rope_rotate_chunk_f(u32x4& x1, u32x4& x2, int64_t pos,
-                                                    const double (&fr)[8]) {
-  float c[8], s[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) rope_cs(pos, fr[r], c[r], s[r]);
-  rotate_chunk(x1, x2, c, s);
-}
 
 // Rotation of one chunk pair at `pos` for frequencies i0 .. i0+7.
 __device__ __forceinline__ void rope_rotate_chunk(u32x4& x1, u32x4& x2, int64_t pos,

@@ -25,19 +25,34 @@ namespace dbsa {
 // ---------------------------------------------------------------------------
 // Gather + re-RoPE (materialised).
 // ---------------------------------------------------------------------------
+// bf16: positions p = 64 t + r are rotated by the angle sum of 64 t (shared by
+// the block's tokens, which all lie in one 64-aligned tile) and r, exactly as
+// the query kernel rotates pool rows, so both paths round identically.
 template <int D>
 __global__ __launch_bounds__(256) void k_gather_bf16(GatherArgs a) {
-  constexpr int CP = D / 16;
+  constexpr int CP = D / 16, H = D / 2;
   constexpr int TOK = 256 / CP;
+  static_assert(kKeyTile % TOK == 0, "a block's tokens share one 64-row tile");
+  __shared__ float tile_c[H], tile_s[H];
   const int b = blockIdx.y;
   const int u = blockIdx.x * TOK + threadIdx.x / CP;
   const int c = threadIdx.x % CP;
+  if (threadIdx.x < H) {
+    const int64_t base = (int64_t)(blockIdx.x * TOK) & ~(int64_t)(kKeyTile - 1);
+    rope_cs(base, a.freq.rev[threadIdx.x], tile_c[threadIdx.x], tile_s[threadIdx.x]);
+  }
+  __syncthreads();
   const int32_t* st = a.start + (int64_t)b * (a.n_ids + 1);
   if (u >= st[a.n_ids]) return;
   const int i = upper_index(st, a.n_ids, u);
   const int64_t src_tok = a.src[(int64_t)b * a.n_ids + i] + (u - st[i]);
   float cs[8], sn[8];
-  rope_cs8(u, a.freq, 8 * c, cs, sn);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float cr, sr;
+    rope_cs(u & (kKeyTile - 1), a.freq.rev[8 * c + r], cr, sr);
+    angle_add(tile_c[8 * c + r], tile_s[8 * c + r], cr, sr, cs[r], sn[r]);
+  }
   const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_pool);
   const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_pool);
   u32x4* ko = reinterpret_cast<u32x4*>(a.k_out);
@@ -150,7 +165,13 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   static_assert((2 * INSTR) % NW == 0, "loads must split evenly over the waves");
   static_assert((64 * NW) % CP == 0, "each thread keeps one chunk pair");
   constexpr uint8_t kRot = 1, kNew = 2;
+  constexpr int H = D / 2;
+  // Rotation work items (row, chunk pair) per thread; each thread keeps the
+  // angles of its fixed row offsets in registers when it has at most two.
+  constexpr int IPT = (kKeyTile * CP + 64 * NW - 1) / (64 * NW);
+  constexpr bool KEEP_B = IPT <= 2;
   __shared__ __align__(16) char lds[NST * Gm::STAGE];
+  __shared__ __align__(16) f32x2 rot_a[NST][kMaxHalf];  // cos / sin of w_i * u0 per stage
   __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
   __shared__ uint64_t row_k[NST][kKeyTile], row_v[NST][kKeyTile];
   __shared__ int32_t row_dst[NST][kKeyTile];
@@ -214,6 +235,7 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
   const int64_t tok0_1 = (int64_t)b * a.cap, tok0_2 = (int64_t)b * a.n_new;
 
+  const double fa = a.freq.rev[lane % H];  // wavefront 0: tile angle of frequency `lane`
   // Row sources of local tile li (wavefront 0, one row per lane).  The tile
   // flags are double-buffered over 8 tiles: a slow wavefront may still read
   // tile li-1's flag while tile li+3's is being written.
@@ -237,6 +259,11 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
       const uint8_t f = real ? (buf != 1 ? kRot : 0) | (buf == 2 ? kNew : 0) : 0;
       row_flag[slot][lane] = f;
       row_dst[slot][lane] = dst0 + (int)tok;
+      if (lane < H) {
+        float c, sn;
+        rope_cs((int64_t)(it0 + li) * kKeyTile, fa, c, sn);
+        rot_a[slot][lane] = f32x2{c, sn};
+      }
       const uint64_t any_rot = __builtin_amdgcn_ballot_w64(f & kRot);
       const uint64_t any_new = __builtin_amdgcn_ballot_w64(f & kNew);
       if (lane == 0) tile_flag[li & (2 * NST - 1)] = (any_rot ? kRot : 0) | (any_new ? kNew : 0);
@@ -271,59 +298,97 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   int koff[KS], vbase[OT];
   lane_offsets16<D>(lane, kh * KH, koff, vbase);
   // The in-LDS rotation handles chunk pair tid % CP of its rows: its 8
-  // frequencies live in registers (no per-lane kernel-argument loads in the
-  // loop, whose vector-memory counter is reserved for the tile loads).
+  // frequencies, and the angles of its fixed row offsets, live in registers
+  // (no per-lane kernel-argument loads in the loop, whose vector-memory
+  // counter is reserved for the tile loads).
   double fr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (tid % CP) + i];
+  float rb_c[KEEP_B ? IPT : 1][8], rb_s[KEEP_B ? IPT : 1][8];
+  if constexpr (KEEP_B) {
+#pragma unroll
+    for (int k = 0; k < IPT; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rope_cs(((tid + k * 64 * NW) / CP) & (kKeyTile - 1), fr[i], rb_c[k][i], rb_s[k][i]);
+  }
   const bool writer = rg == 0;  // one row group writes the new tokens back
+
+  // RoPE at the virtual position for pool rows and new tokens of local tile
+  // li, in LDS; the new tokens' rotated K (from registers) and V go to the
+  // context buffer.  Runs one tile ahead of the attention (see the loop).
+  auto rotate = [&](int li) {
+    const int slot = li % NST;
+    if (!(tile_flag[li & (2 * NST - 1)] & kRot)) return;
+    char* st = lds + slot * Gm::STAGE;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int uidx = tid + k * 64 * NW;
+      if (uidx >= kKeyTile * CP) break;
+      const int row = uidx / CP, c = uidx - row * CP;
+      const uint8_t f = row_flag[slot][row];
+      if (!(f & kRot)) continue;
+      u32x4* k1 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c) * 16);
+      u32x4* k2 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c + CP) * 16);
+      u32x4 x1 = *k1, x2 = *k2;
+      // angle(u0 + row) = angle(u0) (tile table) + angle(row) (registers).
+      float cs[8], sn[8];
+      const f32x4* ap = reinterpret_cast<const f32x4*>(&rot_a[slot][8 * c]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 av = ap[h];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * h + e;
+          float cb, sb;
+          if constexpr (KEEP_B) {
+            cb = rb_c[k][i];
+            sb = rb_s[k][i];
+          } else {
+            rope_cs(row, fr[i], cb, sb);
+          }
+          angle_add(av[2 * e], av[2 * e + 1], cb, sb, cs[i], sn[i]);
+        }
+      }
+      rotate_chunk(x1, x2, cs, sn);
+      *k1 = x1;
+      *k2 = x2;
+      if ((f & kNew) && writer) {
+        const int64_t d = (((int64_t)b * a.cap + row_dst[slot][row]) * a.hkv + g) * CR;
+        u32x4* ko = static_cast<u32x4*>(a.k_ctx);
+        u32x4* vo = static_cast<u32x4*>(a.v_ctx);
+        const char* vs = st + Gm::KBYTES + row * Gm::ROW;
+        ko[d + c] = x1;
+        ko[d + c + CP] = x2;
+        vo[d + c] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c) * 16);
+        vo[d + c + CP] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c + CP) * 16);
+      }
+    }
+  };
 
   for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
   waitcnt<0, 0>();
   barrier_nofence();
   for (int li = 0; li < NST - 1 && li < cnt; ++li) load(li);
+  if (cnt > 0) {
+    wait_vm<true>(LPW * min(NST - 2, cnt - 1));  // tile 0 landed
+    barrier_nofence();
+    rotate(0);
+  }
   for (int li = 0; li < cnt; ++li) {
     if (li + NST - 1 < cnt) plan(li + NST - 1);
-    // Tile li landed (only the younger tiles' loads may fly); the barrier also
-    // publishes the new address table and frees the stage refilled below.
-    wait_vm<true>(LPW * min(NST - 2, cnt - 1 - li));
+    // Tile li+1 landed (only tile li+2's loads may fly; LDS writes are done
+    // too); the barrier then publishes tile li's rotation and the new address
+    // table, and frees tile li-1's stage for the refill below.  Tile li+1 is
+    // rotated while tile li is attended: two different stages.
+    wait_vm<true>(LPW * max(0, min(NST - 3, cnt - 2 - li)));
     barrier_nofence();
     if (li + NST - 1 < cnt) load(li + NST - 1);
-    const int slot = li % NST;
-    char* st = lds + slot * Gm::STAGE;
-    const int u0 = (it0 + li) * kKeyTile;
-    const uint8_t tf = tile_flag[li & (2 * NST - 1)];
-    if (tf & kRot) {
-      // RoPE at the virtual position for pool rows and new tokens; the new
-      // tokens' rotated K (from registers) and V go to the context buffer.
-      for (int uidx = tid; uidx < kKeyTile * CP; uidx += 64 * NW) {
-        const int row = uidx / CP, c = uidx - row * CP;
-        const uint8_t f = row_flag[slot][row];
-        if (!(f & kRot)) continue;
-        u32x4* k1 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c) * 16);
-        u32x4* k2 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c + CP) * 16);
-        u32x4 x1 = *k1, x2 = *k2;
-        rope_rotate_chunk_f(x1, x2, u0 + row, fr);
-        *k1 = x1;
-        *k2 = x2;
-        if ((f & kNew) && writer) {
-          const int64_t d = (((int64_t)b * a.cap + row_dst[slot][row]) * a.hkv + g) * CR;
-          u32x4* ko = static_cast<u32x4*>(a.k_ctx);
-          u32x4* vo = static_cast<u32x4*>(a.v_ctx);
-          const char* vs = st + Gm::KBYTES + row * Gm::ROW;
-          ko[d + c] = x1;
-          ko[d + c + CP] = x2;
-          vo[d + c] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c) * 16);
-          vo[d + c + CP] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c + CP) * 16);
-        }
-      }
-      waitcnt<63, 0>();
-      barrier_nofence();
-    }
+    if (li + 1 < cnt) rotate(li + 1);
     if (wave_live) {
-      const int k0 = u0 + kh * KH;
+      const int k0 = (it0 + li) * kKeyTile + kh * KH;
       const int lim = qpos - k0;  // keys kr <= lim are visible (causal over new tokens)
-      fl.template tile<KH>(st, koff, vbase, qb, k0 + KH - 1 > pos0,
+      fl.template tile<KH>(lds + (li % NST) * Gm::STAGE, koff, vbase, qb, k0 + KH - 1 > pos0,
                            [=](int kr) { return kr <= lim; });
     }
   }
