@@ -50,7 +50,7 @@ def visible_pairs(lens, sink, j):
 
 
 def executed_tiles(lens, sink, j):
-    """64-key tiles the prefill walks, summed over 128-row query tiles."""
+    """64-key tiles the prefill walks, summed over 256-row query tiles."""
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     n = int(off[-1])
     nb = len(lens)
@@ -302,7 +302,8 @@ def main():
                      "ms_per_launch": ms_prefill,
                      "algorithmic_flop_per_launch": exact_flop},
         "prefill": {"exact_pairs_per_head": pairs, "exact_TFLOP": exact_flop / 1e12,
-                    "executed_tiles_128x64_per_head": tiles,
+                    "executed_tiles_per_head": tiles,
+                    "tile_rows_x_keys": [ROW_TILE, KEY_TILE],
                     "executed_tile_TFLOP": tile_flop / 1e12,
                     "exact_TFLOP/s": exact_flop / (ms_prefill * 1e-3) / 1e12,
                     "executed_tile_TFLOP/s": tile_flop / (ms_prefill * 1e-3) / 1e12},

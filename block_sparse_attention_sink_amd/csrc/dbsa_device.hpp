@@ -171,6 +171,14 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16 s) {
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.0f;
 
+constexpr int kScorePrefetch = 2;  // k-steps of K fragments requested ahead
+
+// Placed first in the body of a rarely taken, wave-uniform branch: a volatile
+// asm cannot be speculated, so the compiler keeps a real branch instead of
+// if-converting the body into selects that every tile would then execute (the
+// element mask of partly visible tiles and the softmax reference raise).
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 template <int D>
 struct Flash {
   static constexpr int KS = D / 16;  // k-steps over the head dim
@@ -189,6 +197,10 @@ struct Flash {
   }
 
   // S^T of one tile relative to the current reference m (K fragments from LDS).
+  // The fragments of k-step ks + PF are requested before the two MFMAs of
+  // k-step ks, so the LDS latency hides behind matrix work instead of
+  // stalling every k-step.
+  static constexpr int PF = kScorePrefetch;
   __device__ __forceinline__ void scores(const char* st, const int (&koff)[KS],
                                          const bf16x8 (&qb)[KS], f32x16& s0, f32x16& s1) const {
 #pragma unroll
@@ -196,12 +208,23 @@ struct Flash {
       s0[i] = -m;
       s1[i] = -m;
     }
+    bf16x8 ka[PF + 1][2];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) {
+      ka[ks][0] = *reinterpret_cast<const bf16x8*>(st + koff[ks]);
+      ka[ks][1] = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 32 * Gm::KROW);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(st + koff[ks]);
-      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 32 * Gm::KROW);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
+      if (ks + PF < KS) {
+        ka[(ks + PF) % (PF + 1)][0] = *reinterpret_cast<const bf16x8*>(st + koff[ks + PF]);
+        ka[(ks + PF) % (PF + 1)][1] =
+            *reinterpret_cast<const bf16x8*>(st + koff[ks + PF] + 32 * Gm::KROW);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (PF + 1)][0], qb[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (PF + 1)][1], qb[ks], s1, 0, 0, 0);
+      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     // 2 MFMA
     }
   }
 
@@ -210,6 +233,7 @@ struct Flash {
   template <typename Vis>
   __device__ __forceinline__ void head(f32x16& s0, f32x16& s1, bool mask, Vis vis) {
     if (mask) {
+      keep_branch();
       const int hh = (threadIdx.x >> 5) & 1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -224,6 +248,7 @@ struct Flash {
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
     const bool need = mx > kLazy || (!have && mx > kNegInf);
     if (__builtin_amdgcn_ballot_w64(need)) {
+      keep_branch();
       const float delta = need ? mx : 0.0f;
       const float alpha = have ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
       m += delta;
@@ -460,6 +485,7 @@ struct Flash16 {
       }
     const int q = (threadIdx.x >> 4) & 3;
     if (mask) {
+      keep_branch();
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -474,6 +500,7 @@ struct Flash16 {
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
     const bool need = mx > kLazy || (!have && mx > kNegInf);
     if (__builtin_amdgcn_ballot_w64(need)) {
+      keep_branch();
       const float delta = need ? mx : 0.0f;
       const float alpha = have ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
       m += delta;
