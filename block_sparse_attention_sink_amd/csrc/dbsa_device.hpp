@@ -147,6 +147,37 @@ struct TileGeom {
   }
 };
 
+// This lane's value and its partner's 32 (or 16) lanes away, ordered (lower
+// lane's, upper lane's) in both lanes, by one v_permlane32_swap (or
+// v_permlane16_swap): a vector instruction, where a shuffle would be an LDS
+// permute queued behind the tile reads of the other wavefront on the SIMD.
+__device__ __forceinline__ f32x2 pair_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const f32x2 h = pair_xor32(x);
+  return __builtin_fmaxf(h[0], h[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const f32x2 h = pair_xor16(x);
+  return __builtin_fmaxf(h[0], h[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const f32x2 h = pair_xor32(x);
+  return h[0] + h[1];
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const f32x2 h = pair_xor16(x);
+  return h[0] + h[1];
+}
+
 // Eight probabilities of one MFMA result (registers B .. B+7) as a bf16 B operand.
 template <int B>
 __device__ __forceinline__ bf16x8 pack_p(const f32x16 s) {
@@ -171,19 +202,32 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16 s) {
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.0f;
 
-constexpr int kScorePrefetch = 2;  // k-steps of K fragments requested ahead
-
 // Placed first in the body of a rarely taken, wave-uniform branch: a volatile
 // asm cannot be speculated, so the compiler keeps a real branch instead of
 // if-converting the body into selects that every tile would then execute (the
 // element mask of partly visible tiles and the softmax reference raise).
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedTrans = 0x400;
+
+// The vector work of one tile (mask, maximum, exponentials, packing, row sum)
+// is a chain of dependent instructions whose latency a single wavefront cannot
+// hide; the tile loop therefore interleaves it, instruction group by group,
+// with matrix work that does not depend on it:
+//   pv_head  O += V^T P^T of the previous tile, with the mask and row maximum
+//            of the current tile (and the rare reference raise after it);
+//   exp_next P = 2^S of the current tile, its bf16 packing and row sum, with
+//            the next tile's S^T = K Q^T (accumulators started at -m, the
+//            reference just settled).
 template <int D>
 struct Flash {
   static constexpr int KS = D / 16;  // k-steps over the head dim
   static constexpr int OT = D / 32;  // O^T row tiles
+  static constexpr int NPV = 4 * OT;  // P V products per tile (4 k-steps of 16 keys x OT)
   using Gm = TileGeom<D>;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
   f32x16 o[OT];
   float m, l;
   bool have;
@@ -196,42 +240,56 @@ struct Flash {
     have = false;
   }
 
-  // S^T of one tile relative to the current reference m (K fragments from LDS).
-  // The fragments of k-step ks + PF are requested before the two MFMAs of
-  // k-step ks, so the LDS latency hides behind matrix work instead of
-  // stalling every k-step.
-  static constexpr int PF = kScorePrefetch;
-  __device__ __forceinline__ void scores(const char* st, const int (&koff)[KS],
+  // A operand of P V product j (k-step kk = j / OT, O^T rows 32t, t = j % OT):
+  // two transposed reads of the natural V tile, keys 16kk + 4h + 0..3 and
+  // 16kk + 8 + 4h + 0..3 at head dim 32t + col -- the key order in which the
+  // S^T result layout hands out P (see pack_p).
+  __device__ __forceinline__ bf16x8 vfrag(const char* st_v, const int (&vbase)[OT], int j) const {
+    const char* a0 = st_v + vbase[j % OT] + (16 * (j / OT)) * Gm::ROW;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(a0 + 8 * Gm::ROW));
+    const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v8);
+  }
+  // K fragment of k-step ks, rows h*32 .. +31 of the tile.
+  __device__ __forceinline__ bf16x8 kfrag(const char* st_k, const int (&koff)[KS], int ks, int h) const {
+    return *reinterpret_cast<const bf16x8*>(st_k + koff[ks] + h * 32 * Gm::KROW);
+  }
+
+  // S^T of one tile relative to the current reference m (no interleaving).
+  __device__ __forceinline__ void scores(const char* st_k, const int (&koff)[KS],
                                          const bf16x8 (&qb)[KS], f32x16& s0, f32x16& s1) const {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s0[i] = -m;
       s1[i] = -m;
     }
-    bf16x8 ka[PF + 1][2];
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) {
-      ka[ks][0] = *reinterpret_cast<const bf16x8*>(st + koff[ks]);
-      ka[ks][1] = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 32 * Gm::KROW);
-    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) {
-        ka[(ks + PF) % (PF + 1)][0] = *reinterpret_cast<const bf16x8*>(st + koff[ks + PF]);
-        ka[(ks + PF) % (PF + 1)][1] =
-            *reinterpret_cast<const bf16x8*>(st + koff[ks + PF] + 32 * Gm::KROW);
-      }
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (PF + 1)][0], qb[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (PF + 1)][1], qb[ks], s1, 0, 0, 0);
-      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     // 2 MFMA
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(st_k, koff, ks, 0), qb[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(st_k, koff, ks, 1), qb[ks], s1, 0, 0, 0);
     }
   }
 
-  // Mask (when `mask`: key kr of the tile is kept iff vis(kr)), row maximum and
-  // the rare reference raise (rescaling o and l).  Leaves s = S - m.
-  template <typename Vis>
-  __device__ __forceinline__ void head(f32x16& s0, f32x16& s1, bool mask, Vis vis) {
+  // O^T += V^T P^T of one tile (no interleaving).
+  __device__ __forceinline__ void pv(const char* st_v, const int (&vbase)[OT], const bf16x8 (&p)[4]) {
+#pragma unroll
+    for (int j = 0; j < NPV; ++j)
+      o[j % OT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(st_v, vbase, j), p[j / OT],
+                                                          o[j % OT], 0, 0, 0);
+  }
+
+  // Mask (when `mask`: key kr of the tile is kept iff vis(kr)), row maximum
+  // and the rare reference raise (rescaling o and l); leaves s = S - m.  When
+  // PV, the previous tile's O^T += V^T P^T (V from st_v, probabilities p) is
+  // issued in 16 groups, fenced against the scheduler: group j holds P V
+  // product j (its fragments were read two groups earlier) and one step of
+  // the maximum tree.
+  template <bool PV, typename Vis>
+  __device__ __forceinline__ void pv_head(const char* st_v, const int (&vbase)[OT],
+                                          const bf16x8 (&p)[4], f32x16& s0, f32x16& s1, bool mask,
+                                          Vis vis) {
     if (mask) {
       keep_branch();
       const int hh = (threadIdx.x >> 5) & 1;
@@ -242,10 +300,38 @@ struct Flash {
         s1[i] = vis(kr + 32) ? s1[i] : kNegInf;
       }
     }
-    float mx = kNegInf;
+    float mq[8];
+    // Maximum-tree step j: pairs of four scores for j < 8, then the tree.
+    auto max_step = [&](int j) {
+      if (j < 8) {
+        mq[j] = __builtin_fmaxf(__builtin_fmaxf(s0[2 * j], s0[2 * j + 1]),
+                                __builtin_fmaxf(s1[2 * j], s1[2 * j + 1]));
+      } else if (j < 12) {
+        mq[j - 8] = __builtin_fmaxf(mq[j - 8], mq[j - 4]);
+      } else if (j < 14) {
+        mq[j - 12] = __builtin_fmaxf(mq[j - 12], mq[j - 10]);
+      } else if (j == 14) {
+        mq[0] = __builtin_fmaxf(mq[0], mq[1]);
+      }
+    };
+    if constexpr (PV) {
+      bf16x8 va[3];
+      va[0] = vfrag(st_v, vbase, 0);
+      va[1] = vfrag(st_v, vbase, 1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      for (int j = 0; j < NPV; ++j) {
+        if (j + 2 < NPV) va[(j + 2) % 3] = vfrag(st_v, vbase, j + 2);
+        o[j % OT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j % 3], p[j / OT], o[j % OT], 0, 0, 0);
+        max_step(j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = NPV; j < 15; ++j) max_step(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 15; ++j) max_step(j);
+    }
+    const float mx = max_xor32(mq[0]);
     const bool need = mx > kLazy || (!have && mx > kNegInf);
     if (__builtin_amdgcn_ballot_w64(need)) {
       keep_branch();
@@ -266,106 +352,104 @@ struct Flash {
     }
   }
 
-  // P = 2^s packed to bf16, row sum added to l.  When NEXT, the S^T MFMAs of
-  // the next tile (K fragments from st_next) are issued interleaved with this
-  // VALU work, so the wave's instruction stream alternates matrix and vector
-  // instructions; the next tile's scores use the reference m just settled.
-  template <bool NEXT>
-  __device__ __forceinline__ void probs(f32x16& s0, f32x16& s1, bf16x8 (&p)[4],
-                                        const char* st_next, const int (&koff)[KS],
-                                        const bf16x8 (&qb)[KS], f32x16& n0, f32x16& n1) {
-    if constexpr (NEXT) {
+  // P = 2^s packed to bf16 into p, row sum added to l; the next tile's
+  // S^T = K Q^T - m (K from st_k) goes to n0 / n1.  Issued in KS groups,
+  // fenced against the scheduler.  The first half of the groups holds the
+  // exponentials of s0 and the MFMAs of n1 (key rows 32..63), the second half
+  // those of s1 and n0 (key rows 0..31), so n0 can take the registers of s0;
+  // each group also packs and sums the pairs whose exponentials the group
+  // before it issued.
+  __device__ __forceinline__ void exp_next(const char* st_k, const int (&koff)[KS],
+                                           const bf16x8 (&qb)[KS], f32x16& s0, f32x16& s1,
+                                           bf16x8 (&p)[4], f32x16& n0, f32x16& n1) {
+    static_assert(KS == 8 || KS == 4, "head dim 128 or 64");
+    constexpr int H = KS / 2;    // groups per half
+    constexpr int PPG = 8 / H;   // score pairs of one half per group
+    uint32_t w0[8], w1[8];
+    float sq0[8], sq1[8];
+    auto fin0 = [&](int u) {
+      w0[u] = pack_bf16x2(s0[2 * u], s0[2 * u + 1]);
+      sq0[u] = s0[2 * u] + s0[2 * u + 1];
+    };
+    auto fin1 = [&](int u) {
+      w1[u] = pack_bf16x2(s1[2 * u], s1[2 * u + 1]);
+      sq1[u] = s1[2 * u] + s1[2 * u + 1];
+    };
+    // Group x: MFMAs of k-steps 2x, 2x + 1 of one accumulator.
+    bf16x8 ka[2][2];
+    auto kread = [&](int x, int h, int b) {
+      ka[b][0] = kfrag(st_k, koff, (2 * x) % KS, h);
+      ka[b][1] = kfrag(st_k, koff, (2 * x + 1) % KS, h);
+    };
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        n0[i] = -m;
-        n1[i] = -m;
+    for (int i = 0; i < 16; ++i) n1[i] = -m;
+    kread(0, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+      const bool second = x >= H;
+      if (x + 1 < KS) kread(x + 1, x + 1 >= H ? 0 : 1, (x + 1) & 1);
+      if (x == H) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) n0[i] = -m;
       }
-    }
-    // 8 rounds: 2 next-tile MFMAs (one k-step) + 4 exponentials each.
+      const int k0 = (2 * x) % KS, k1 = (2 * x + 1) % KS;
+      if (!second) {
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][0], qb[k0], n1, 0, 0, 0);
+      } else {
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][0], qb[k0], n0, 0, 0, 0);
+      }
+      const int xh = second ? x - H : x;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if constexpr (NEXT) {
-        if (r < KS) {
-          const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(st_next + koff[r]);
-          const bf16x8 ka1 =
-              *reinterpret_cast<const bf16x8*>(st_next + koff[r] + 32 * Gm::KROW);
-          n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[r], n0, 0, 0, 0);
-          n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[r], n1, 0, 0, 0);
+      for (int e = 0; e < PPG; ++e) {
+        const int pr = xh * PPG + e;
+        if (!second) {
+          s0[2 * pr] = __builtin_amdgcn_exp2f(s0[2 * pr]);
+          s0[2 * pr + 1] = __builtin_amdgcn_exp2f(s0[2 * pr + 1]);
+        } else {
+          s1[2 * pr] = __builtin_amdgcn_exp2f(s1[2 * pr]);
+          s1[2 * pr + 1] = __builtin_amdgcn_exp2f(s1[2 * pr + 1]);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = 2 * r + e;
-        s0[i] = __builtin_amdgcn_exp2f(s0[i]);
-        s1[i] = __builtin_amdgcn_exp2f(s1[i]);
+      if (!second) {
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][1], qb[k1], n1, 0, 0, 0);
+      } else {
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][1], qb[k1], n0, 0, 0, 0);
       }
-      if constexpr (NEXT) {
-        if (r < KS) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
+      if (x > 0)
+#pragma unroll
+        for (int e = 0; e < PPG; ++e) {
+          const int xp = x - 1;
+          if (xp < H) fin0((xp) * PPG + e);
+          else fin1((xp - H) * PPG + e);
         }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    p[0] = pack_p<0>(s0);
-    p[1] = pack_p<8>(s0);
-    p[2] = pack_p<0>(s1);
-    p[3] = pack_p<8>(s1);
-    float ra = 0.0f, rb = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ra += s0[i];
-      rb += s1[i];
-    }
-    l += ra + rb;
-  }
-
-  // O^T += V^T P^T.  The A operand of k-step kk for O^T rows 32t..32t+31 is
-  // read from the natural V tile with two transposed reads: keys
-  // 16kk + 4h + 0..3 and 16kk + 8 + 4h + 0..3 at head dim 32t + col, the key
-  // order in which the S^T result layout hands out P (see pack_p).
-  __device__ __forceinline__ void pv(const char* st, const int (&vbase)[OT],
-                                     const bf16x8 (&p)[4]) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    for (int e = 0; e < PPG; ++e) fin1((H - 1) * PPG + e);
+    float sq[8];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int k = 0; k < 8; ++k) sq[k] = sq0[k] + sq1[k];
 #pragma unroll
-      for (int t = 0; t < OT; ++t) {
-        const char* a0 = st + vbase[t] + (16 * kk) * Gm::ROW;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a0 + 8 * Gm::ROW));
-        const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
-                                                              hi[0], hi[1], hi[2], hi[3]};
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), p[kk],
-                                                       o[t], 0, 0, 0);
-      }
-  }
-
-  // One whole tile without cross-tile pipelining.
-  template <typename Vis>
-  __device__ __forceinline__ void tile(const char* st, const int (&koff)[KS],
-                                       const int (&vbase)[OT], const bf16x8 (&qb)[KS], bool mask,
-                                       Vis vis) {
-    f32x16 s0, s1, n0, n1;
-    bf16x8 p[4];
-    scores(st, koff, qb, s0, s1);
-    head(s0, s1, mask, vis);
-    probs<false>(s0, s1, p, st, koff, qb, n0, n1);
-    pv(st, vbase, p);
+    for (int w = 4; w > 0; w >>= 1)
+#pragma unroll
+      for (int k = 0; k < w; ++k) sq[k] += sq[k + w];
+    l += sq[0];
+    p[0] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
+    p[1] = __builtin_bit_cast(bf16x8, u32x4{w0[4], w0[5], w0[6], w0[7]});
+    p[2] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
+    p[3] = __builtin_bit_cast(bf16x8, u32x4{w1[4], w1[5], w1[6], w1[7]});
   }
 
   // Row sum over both lane halves (call once, all lanes).
-  __device__ __forceinline__ float total() const { return l + __shfl_xor(l, 32); }
+  __device__ __forceinline__ float total() const { return sum_xor32(l); }
 };
 
-// This lane's fragment offsets inside a stage (see Flash::scores / pv).
-// koff[ks]: K row col, logical chunk 2ks + hh.  vbase[t]: the address this
-// lane presents to the transposed V read for O^T rows 32t..: row 4h + q
-// (q = (lane % 16) / 4), head dims 32t + 16 ((lane / 16) % 2) + 4 (lane % 4).
+// This lane's fragment offsets inside a tile (see Flash::kfrag / vfrag).
+// koff[ks]: K row col, logical chunk 2ks + hh, from the K tile start.
+// vbase[t]: from the V tile start, the address this lane presents to the
+// transposed V read for O^T rows 32t..: row 4h + q (q = (lane % 16) / 4),
+// head dims 32t + 16 ((lane / 16) % 2) + 4 (lane % 4).
 template <int D>
 __device__ __forceinline__ void lane_offsets(int lane, int (&koff)[D / 16], int (&vbase)[D / 32]) {
   using Gm = TileGeom<D>;
@@ -377,7 +461,7 @@ __device__ __forceinline__ void lane_offsets(int lane, int (&koff)[D / 16], int 
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
     const int elem = 32 * t + 16 * b + 4 * (lane & 3);
-    vbase[t] = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, elem >> 3) * 16 + (elem & 7) * 2;
+    vbase[t] = row * Gm::ROW + Gm::v_phys(row, elem >> 3) * 16 + (elem & 7) * 2;
   }
 }
 
@@ -417,22 +501,29 @@ __device__ __forceinline__ void waitcnt() {
 }
 
 // Wait until at most n of this wave's vector-memory loads are outstanding
-// (wave-uniform n in {0, 1, 2, 4, 8, 12, 16, 24, 32}); loads complete in issue
-// order, so this waits for all but the n most recent.  LGKM0 additionally
-// waits for this wave's LDS operations.
+// (wave-uniform n >= 0; values above 12 other than 16, 24 and 32 wait for
+// fewer, which is always safe); loads complete in issue order, so this waits
+// for all but the n most recent.  LGKM0 additionally waits for this wave's
+// LDS operations.
 template <bool LGKM0 = false>
 __device__ __forceinline__ void wait_vm(int n) {
   constexpr int L = LGKM0 ? 0 : 15;
   switch (n) {
     case 1: waitcnt<1, L>(); break;
     case 2: waitcnt<2, L>(); break;
+    case 3: waitcnt<3, L>(); break;
     case 4: waitcnt<4, L>(); break;
+    case 5: waitcnt<5, L>(); break;
+    case 6: waitcnt<6, L>(); break;
+    case 7: waitcnt<7, L>(); break;
     case 8: waitcnt<8, L>(); break;
-    case 12: waitcnt<12, L>(); break;
-    case 16: waitcnt<16, L>(); break;
-    case 24: waitcnt<24, L>(); break;
-    case 32: waitcnt<32, L>(); break;
-    default: waitcnt<0, L>(); break;
+    case 9: waitcnt<9, L>(); break;
+    case 10: waitcnt<10, L>(); break;
+    case 11: waitcnt<11, L>(); break;
+    case 12: case 13: case 14: case 15: waitcnt<12, L>(); break;
+    case 16: case 17: case 18: case 19: case 20: case 21: case 22: case 23: waitcnt<16, L>(); break;
+    case 24: case 25: case 26: case 27: case 28: case 29: case 30: case 31: waitcnt<24, L>(); break;
+    default: if (n >= 32) waitcnt<32, L>(); else waitcnt<0, L>(); break;
   }
 }
 
@@ -496,8 +587,7 @@ struct Flash16 {
     for (int j = 0; j < NJ; ++j)
       mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(s[j][0], s[j][1]),
                                                __builtin_fmaxf(s[j][2], s[j][3])));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const bool need = mx > kLazy || (!have && mx > kNegInf);
     if (__builtin_amdgcn_ballot_w64(need)) {
       keep_branch();
@@ -553,8 +643,7 @@ struct Flash16 {
 
   // Row sum over the four lane groups (call once, all lanes).
   __device__ __forceinline__ float total() const {
-    float t = l + __shfl_xor(l, 16);
-    return t + __shfl_xor(t, 32);
+    return sum_xor32(sum_xor16(l));
   }
 };
 

@@ -16,7 +16,7 @@ constexpr int kKeyTile = 64;      // keys per K/V tile (one LDS stage)
 constexpr int kRowsPerWave = 32;  // query rows per wavefront (MFMA N dimension)
 constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
-constexpr int kPrefillStages = 4;  // LDS ring of K/V tiles (3 tiles of lookahead)
+constexpr int kPrefillStages = 4;  // LDS stages per K ring and per V ring
 constexpr int kMaxSegments = 512;  // context segments per batch row in Stage 2
 constexpr int kMaxHalf = 64;       // head_dim / 2 upper bound (head_dim <= 128)
 

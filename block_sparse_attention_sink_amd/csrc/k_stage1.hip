@@ -19,7 +19,8 @@
 namespace dbsa {
 
 // ---------------------------------------------------------------------------
-// K rotation into tile images (the LDS byte images, see TileGeom).
+// K rotation into tile images (the LDS byte images, see TileGeom).  One
+// workgroup per (key tile slot, KV head); keys past the pool are zero.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
@@ -48,16 +49,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
 //
 // Workgroup = 8 wavefronts = 256 query rows of one query head; wave w owns
 // rows r0 + 32w .. +31 (lane layout: see Flash).  The workgroup walks the
-// 64-key tiles that meet its rows' visible intervals through a ring of 4 LDS
-// stages filled by direct global->LDS loads, 3 tiles ahead of the compute.
+// 64-key tiles that meet its rows' visible intervals.  K tiles and V tiles
+// have separate LDS rings of 4 stages, filled by direct global->LDS loads
+// two tiles at a time (see the loop).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillArgs a) {
   using Gm = TileGeom<D>;
   constexpr int KS = D / 16;
-  constexpr int NST = kPrefillStages;
-  constexpr int LPW = 2 * Gm::TU4 / 64 / kPrefillWaves;  // loads per wave per tile
-  __shared__ __align__(16) char lds[NST * Gm::STAGE];
+  constexpr int NS = kPrefillStages;
+  static_assert(NS == 4, "two tiles in use and two in flight per ring");
+  __shared__ __align__(16) char lds[NS * (Gm::KBYTES + Gm::VBYTES)];
+  char* const kring = lds;
+  char* const vring = lds + NS * Gm::KBYTES;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
@@ -114,40 +118,114 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   auto slot_of = [&](int kt) {
     return kt < a.sink_tiles ? kt : a.sink_tiles + (kt - a.win_tile0);
   };
-  // Stage tile `it` into LDS stage `buf` without registers: the K image is a
-  // linear copy; V rows come straight from the token-major tensor, each lane
-  // fetching the chunk that belongs at its LDS position.
-  auto load = [&](int it, int buf) {
+  // Tile loads without registers: the K image is a linear copy; V rows come
+  // straight from the token-major tensor, each lane fetching the chunk that
+  // belongs at its LDS position.  Wave w moves the 1 KiB pieces w, w + 8, ...
+  // of each matrix.
+  constexpr int NPW = Gm::TU4 / 64 / kPrefillWaves;
+  static_assert(NPW * 64 * kPrefillWaves == Gm::TU4, "tile pieces split evenly over the waves");
+  // Per-lane offsets (32-bit, to keep registers free): K in 16-byte chunks
+  // from the head's first tile image, V in elements from the first key tile.
+  int kl[NPW], vo[NPW];
+#pragma unroll
+  for (int jj = 0; jj < NPW; ++jj) {
+    const int i = wave + jj * kPrefillWaves;
+    kl[jj] = i * 64 + lane;
+    const int o16 = i * 1024 + lane * 16;
+    const int row = o16 / Gm::ROW;
+    vo[jj] = (row * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8;
+  }
+  // The wave index as a scalar keeps the LDS destinations (M0) scalar.
+  const int wsc = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t vtile = (int64_t)kKeyTile * a.hkv * D;  // elements per key tile of V
+  auto load_k = [&](int it) {
+    char* st = kring + (it % NS) * Gm::KBYTES;
+    const u32x4* kt = kbase + (int64_t)slot_of(tile_of(it)) * Gm::TU4;
+#pragma unroll
+    for (int jj = 0; jj < NPW; ++jj) dma16(kt + kl[jj], st + (wsc + jj * kPrefillWaves) * 1024);
+  };
+  auto load_v = [&](int it) {
+    char* st = vring + (it % NS) * Gm::VBYTES;
     const int kt = tile_of(it);
-    char* st = lds + buf * Gm::STAGE;
-    copy_to_lds(kbase + (int64_t)slot_of(kt) * Gm::TU4, st, Gm::TU4, wave, kPrefillWaves, lane);
-    for (int i = wave; i * 64 < Gm::TU4; i += kPrefillWaves) {
-      const int off = i * 1024 + lane * 16;
-      const int row = off / Gm::ROW, c = Gm::v_phys(row, (off % Gm::ROW) >> 4);
-      const int64_t tok = min(kt * kKeyTile + row, a.n_keys - 1);
-      dma16(vsrc + (tok * a.hkv + g) * D + c * 8, st + Gm::KBYTES + i * 1024);
+    if ((kt + 1) * kKeyTile <= a.n_keys) {
+      const uint16_t* vt = vsrc + kt * vtile;
+#pragma unroll
+      for (int jj = 0; jj < NPW; ++jj) dma16(vt + vo[jj], st + (wsc + jj * kPrefillWaves) * 1024);
+    } else {  // last, partial key tile: rows past the keys repeat the last key (masked)
+#pragma unroll
+      for (int jj = 0; jj < NPW; ++jj) {
+        const int o16 = (wave + jj * kPrefillWaves) * 1024 + lane * 16;
+        const int row = o16 / Gm::ROW;
+        const int64_t tok = min(kt * kKeyTile + row, a.n_keys - 1);
+        dma16(vsrc + (tok * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8,
+              st + (wsc + jj * kPrefillWaves) * 1024);
+      }
     }
+  };
+  // Requests of (even) iteration i: K of tiles i + 3 and i + 4 and V of
+  // tiles i + 1 and i + 2, each when it exists.
+  auto request = [&](int i) {
+    if (i + 3 < n_tiles) load_k(i + 3);
+    if (i + 4 < n_tiles) load_k(i + 4);
+    if (i + 1 < n_tiles) load_v(i + 1);
+    if (i + 2 < n_tiles) load_v(i + 2);
   };
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 
-  // Ring of NST stages: tile it+NST-1 is requested while tile it is computed.
-  for (int p = 0; p < NST - 1 && p < n_tiles; ++p) load(p, p);
-  for (int it = 0; it < n_tiles; ++it) {
-    // Tile `it` has landed once at most the loads of the tiles after it
-    // (issued earlier) are still outstanding; the barrier then also certifies
-    // that every wave is done with the stage refilled below.
-    wait_vm(LPW * min(NST - 2, n_tiles - 1 - it));
-    barrier_nofence();
-    if (it + NST - 1 < n_tiles) load(it + NST - 1, (it + NST - 1) % NST);
+  // Element mask only on tiles some row cannot fully see.
+  const auto full_of = [&](int it) {
     const int k0 = tile_of(it) * kKeyTile;
-    // Element mask only on tiles some row cannot fully see.
-    const bool full = (k0 + kKeyTile - 1 <= r0) &&
-                      (k0 >= lo_last || (a.sink && k0 + kKeyTile <= sink_end));
+    return (k0 + kKeyTile - 1 <= r0) && (k0 >= lo_last || (a.sink && k0 + kKeyTile <= sink_end));
+  };
+  const auto vis_of = [&](int it) {
+    const int k0 = tile_of(it) * kKeyTile;
     const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
-    fl.tile(lds + (it % NST) * Gm::STAGE, koff, vbase, qb, !full,
-            [=](int kr) { return kr <= tt && (kr >= lt || kr < se); });
+    return [=](int kr) { return kr <= tt && (kr >= lt || kr < se); };
+  };
+  const auto kst = [&](int it) { return kring + (it % NS) * Gm::KBYTES; };
+  const auto vst = [&](int it) { return vring + (it % NS) * Gm::VBYTES; };
+
+  // Prologue: K of tiles 0, 1, 2 and V of tile 0, all landed before the
+  // scores of tile 0.
+  for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
+  load_v(0);
+  wait_vm(0);
+  barrier_nofence();
+  f32x16 s0, s1, n0, n1;
+  bf16x8 pr[4];
+  fl.scores(kst(0), koff, qb, s0, s1);
+  // Iteration i computes the softmax of tile i, P V of tile i - 1 and the
+  // scores of tile i + 1 (reading K of tile i + 1, V of tile i - 1).  Even
+  // iterations start with a barrier: every load requested two iterations
+  // earlier has landed (each wave waits for its own, the barrier for all),
+  // and the stages of K tiles i - 1, i and V tiles i - 3, i - 2, which
+  // iterations up to i - 1 read, are refilled for the next two iterations.
+  // Odd iterations run without a barrier, so the two wavefronts of a SIMD
+  // can drift apart.  The last iteration also computes scores, of a stale K
+  // stage; they are never used.
+  const auto sync = [&](int i) {
+    wait_vm(0);
+    barrier_nofence();
+    request(i);
+  };
+  sync(0);
+  fl.template pv_head<false>(vst(0), vbase, pr, s0, s1, !full_of(0), vis_of(0));
+  fl.exp_next(kst(1), koff, qb, s0, s1, pr, n0, n1);
+  // Two iterations per trip (odd, then even) so the score registers
+  // alternate instead of being copied.
+  for (int i = 1; i < n_tiles; i += 2) {
+    fl.template pv_head<true>(vst(i - 1), vbase, pr, n0, n1, !full_of(i), vis_of(i));
+    fl.exp_next(kst(i + 1), koff, qb, n0, n1, pr, s0, s1);
+    if (i + 1 >= n_tiles) break;
+    sync(i + 1);
+    fl.template pv_head<true>(vst(i), vbase, pr, s0, s1, !full_of(i + 1), vis_of(i + 1));
+    fl.exp_next(kst(i + 2), koff, qb, s0, s1, pr, n0, n1);
   }
+  // P V of the last tile (its V may have been requested by the last barrier).
+  wait_vm(0);
+  barrier_nofence();
+  fl.pv(vst(n_tiles - 1), vbase, pr);
 
   const float lsum = fl.total();
   if (t < r1) {
