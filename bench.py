@@ -258,16 +258,18 @@ def main():
         h = lambda t: t.float().cpu().numpy().astype(np.float64)
         qh, kh, vh = h(q), h(k), h(v)
         rng = np.random.default_rng(7)
-        # Rows from every block, sized so the oracle runs about --cpu-seconds.
-        probe = np.sort(rng.choice(n, 32, replace=False))
-        t = time.perf_counter()
-        orc.prefill(qh, kh, vh, lens, sink, j, theta, rows=probe)
-        per_row = (time.perf_counter() - t) / probe.size
-        n_rows = int(np.clip(args.cpu_seconds / max(per_row, 1e-6), 32, 4096))
-        rows = np.sort(rng.choice(n, n_rows, replace=False))
-        t = time.perf_counter()
-        orc.prefill(qh, kh, vh, lens, sink, j, theta, rows=rows)
-        secs = time.perf_counter() - t
+        # Random rows of the whole pool, in batches, until about --cpu-seconds
+        # of oracle time have been spent.
+        order = rng.permutation(n)
+        done, secs = 0, 0.0
+        while secs < args.cpu_seconds and done < min(n, 8192):
+            batch = np.sort(order[done:done + 64])
+            t = time.perf_counter()
+            orc.prefill(qh, kh, vh, lens, sink, j, theta, rows=batch)
+            secs += time.perf_counter() - t
+            done += batch.size
+        rows = order[:done]
+        n_rows = done
         off = np.concatenate([[0], np.cumsum(lens)])
         blk = np.searchsorted(off, rows, side="right") - 1
         lo = off[np.maximum(blk - j, 0)]
