@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-op", choices=["prefill", "gather", "query", "fused", "copy"],
                     help="run only this operation --steps times (for rocprofv3); prints timing")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="time every operation of the five workloads (one JSON line each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DBSA hot path here runs on a single "
@@ -121,6 +123,9 @@ def main():
     dbsa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.all_workloads:
+        run_all_workloads(dev)
+        return
     w = workload(2)
     lens, sink, j, theta = w.block_lens, w.sink, w.j, w.theta
     n, hq, hkv, d = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
@@ -315,6 +320,131 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def run_all_workloads(dev):
+    """Median time of every hot-path operation on the five workloads (caches
+    flushed before each Stage-2 repetition), with its algorithmic rate."""
+    import torch
+    from block_sparse_attention_sink_amd import dbsa
+    from block_sparse_attention_sink_amd.inputs import PATTERNS, randn, workload
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink_acc = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def timed(fn, reps, flush_first=False):
+        ts = []
+        for r in range(reps + 2):
+            if flush_first:
+                sink_acc.add_(flush.sum())
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts[2:]))
+
+    def emit(wl, op, ms, work, unit, **extra):
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+        print(json.dumps({"workload": wl, "op": op, "ms": ms, "rate": rate, "unit": unit,
+                          "frac_of_peak": rate / peak, **extra}), flush=True)
+
+    for k in (1, 2, 3, 4, 5):
+        w = workload(k)
+        lens, d, hq, hkv = w.block_lens, w.head_dim, w.n_q_heads, w.n_kv_heads
+        dt = w.dtype
+        esz = 4 if dt == "f32" else 2
+        n = w.n_tokens
+        patterns = [(nm, PATTERNS[nm]) for nm in w.patterns] or [("dbsa", (w.sink, w.j))]
+        if k != 4:
+            q = randn((n, hq, d), 11, dt, dev)
+            kk = randn((n, hkv, d), 12, dt, dev)
+            vv = randn((n, hkv, d), 13, dt, dev)
+            o = torch.empty_like(q)
+            for nm, (sk, jj) in patterns:
+                jj = len(lens) if jj < 0 else jj
+                flop = 4.0 * d * hq * visible_pairs(lens, sk, jj)
+                ms = timed(lambda: dbsa.dbsa_prefill(q, kk, vv, lens, sk, jj, w.theta, out=o),
+                           5 if k != 5 else 3)
+                emit(w.name, f"prefill[{nm}]", ms, flop, "TFLOP/s",
+                     note="exact visible-pair flop")
+        if w.append_len:
+            la = w.append_len
+            cap = n + la
+            kc = torch.empty((cap, hkv, d), dtype=kk.dtype, device=dev)
+            vc = torch.empty_like(kc)
+            kc[:n].copy_(kk)
+            vc[:n].copy_(vv)
+            qa = randn((la, hq, d), 14, dt, dev)
+            ka = randn((la, hkv, d), 15, dt, dev)
+            va = randn((la, hkv, d), 16, dt, dev)
+            lens_a = np.append(lens, la).astype(np.int32)
+            new_pairs = visible_pairs(lens_a, w.sink, w.j) - visible_pairs(lens, w.sink, w.j)
+            ctx = new_pairs / la
+            flop = 4.0 * d * hq * new_pairs
+            ms = timed(lambda: dbsa.dbsa_append_block(qa, ka, va, kc, vc, lens, w.sink, w.j,
+                                                      w.theta), 5)
+            emit(w.name, "append_block", ms, flop, "TFLOP/s",
+                 note=f"{la} new tokens, {ctx:.0f} visible keys per row on average")
+        if w.n_new == 0:
+            continue
+        layers = w.layers
+        batch = w.batch
+        nn = w.n_new
+        if k == 4:
+            pool_k = [randn((n, hkv, d), 100 + l, dt, dev) for l in range(layers)]
+            pool_v = [randn((n, hkv, d), 200 + l, dt, dev) for l in range(layers)]
+        else:
+            pool_k, pool_v = [kk], [vv]
+        tp = [int(lens[r].sum()) for r in w.ids]
+        qn = randn((batch, nn, hq, d), 21, dt, dev)
+        kn = randn((batch, nn, hkv, d), 22, dt, dev)
+        vn = randn((batch, nn, hkv, d), 23, dt, dev)
+        on = torch.empty_like(qn)
+        steps = max(w.decode_steps, 0)
+        tail_cap = nn + steps
+        kt = torch.empty((batch, tail_cap, hkv, d), dtype=qn.dtype, device=dev)
+        vt = torch.empty_like(kt)
+        kv_bytes = sum(tp) * hkv * d * esz * 2
+        io = (qn.numel() + kn.numel() + vn.numel() + on.numel()) * esz
+
+        def fused_all():
+            for l in range(len(pool_k)):
+                dbsa.dbsa_query_attn_gathered(qn, kn, vn, pool_k[l], pool_v[l], lens, w.ids, kt,
+                                              vt, [0] * batch, w.theta, out=on)
+        ms = timed(fused_all, 5, flush_first=True)
+        emit(w.name, f"fused_gather_query[{len(pool_k)} layers x {batch} x {nn} tokens]", ms,
+             len(pool_k) * (kv_bytes + io), "GB/s",
+             note="unrotated K/V of the gathered blocks read once + Q, new K/V, O")
+        if len(pool_k) == 1:
+            cap = max(tp) + nn + steps
+            kg = torch.empty((batch, cap, hkv, d), dtype=qn.dtype, device=dev)
+            vg = torch.empty_like(kg)
+            ms_g = timed(lambda: dbsa.dbsa_gather_rope(kk, vv, lens, w.ids, w.theta, k_out=kg,
+                                                       v_out=vg), 5, flush_first=True)
+            emit(w.name, "gather_rope", ms_g, 2 * kv_bytes, "GB/s",
+                 note="read + write of the gathered K/V")
+            ms_q = timed(lambda: dbsa.dbsa_query_attn(qn, kn, vn, kg, vg, tp, w.theta, out=on),
+                         5, flush_first=True)
+            emit(w.name, "query_attn", ms_q, kv_bytes + io, "GB/s",
+                 note="rotated K/V of the context read once + Q, new K/V, O")
+        if steps:
+            q1 = randn((batch, 1, hq, d), 31, dt, dev)
+            k1 = randn((batch, 1, hkv, d), 32, dt, dev)
+            v1 = randn((batch, 1, hkv, d), 33, dt, dev)
+            o1 = torch.empty_like(q1)
+
+            def decode():
+                for s in range(steps):
+                    dbsa.dbsa_query_attn_gathered(q1, k1, v1, kk, vv, lens, w.ids, kt, vt,
+                                                  [nn + s] * batch, w.theta, out=o1)
+            ms = timed(decode, 3, flush_first=True)
+            byt = steps * kv_bytes
+            emit(w.name, f"decode[{steps} steps]", ms, byt, "GB/s",
+                 note="per step: the gathered K/V read once (tail tokens not counted)")
 
 
 if __name__ == "__main__":

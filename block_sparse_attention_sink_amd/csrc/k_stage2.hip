@@ -154,21 +154,23 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 // buffer (each new token lies in exactly one tile of one split).
 // ---------------------------------------------------------------------------
 template <int D, int RWW, int KSPL>
-__global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
+__global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
-  constexpr int NW = RWW * KSPL, KH = kKeyTile / KSPL;
+  // RWW x KSPL attention wavefronts, then NL loader wavefronts that plan,
+  // load and rotate the tiles ahead of the attention.
+  constexpr int NWA = RWW * KSPL, NL = kQueryLoaders, NW = NWA + NL, KH = kKeyTile / KSPL;
   constexpr int KS = D / 32, OT = D / 16, CP = D / 16, CR = D / 8;
   constexpr int RW = 16;  // rows per wavefront
   constexpr int NST = 4;
   constexpr int INSTR = Gm::TU4 / 64;  // 1 KiB loads per matrix per tile
-  constexpr int LPW = 2 * INSTR / NW;  // loads per wave per tile
-  static_assert((2 * INSTR) % NW == 0, "loads must split evenly over the waves");
-  static_assert((64 * NW) % CP == 0, "each thread keeps one chunk pair");
+  constexpr int LPW = 2 * INSTR / NL;  // loads per loader wave per tile
+  static_assert((2 * INSTR) % NL == 0, "loads must split evenly over the loader waves");
+  static_assert((64 * NL) % CP == 0, "each loader thread keeps one chunk pair");
   constexpr uint8_t kRot = 1, kNew = 2;
   constexpr int H = D / 2;
   // Rotation work items (row, chunk pair) per thread; each thread keeps the
   // angles of its fixed row offsets in registers when it has at most two.
-  constexpr int IPT = (kKeyTile * CP + 64 * NW - 1) / (64 * NW);
+  constexpr int IPT = (kKeyTile * CP + 64 * NL - 1) / (64 * NL);
   constexpr bool KEEP_B = IPT <= 2;
   __shared__ __align__(16) char lds[NST * Gm::STAGE];
   __shared__ __align__(16) f32x2 rot_a[NST][kMaxHalf];  // cos / sin of w_i * u0 per stage
@@ -179,15 +181,17 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   __shared__ uint8_t tile_flag[2 * NST];  // indexed by tile % 8 (see plan)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int rw = wave % RWW, kh = wave / RWW;  // row wavefront, key half
+  const bool loader = wave >= NWA;
+  const int ltid = tid - 64 * NWA;  // thread index among the loaders
+  const int rw = wave % RWW, kh = loader ? 0 : wave / RWW;  // row wavefront, key half
   const int q16 = (lane >> 4) & 3, r16 = lane & 15;
   const int split = blockIdx.x;
   const int g = blockIdx.y % a.hkv, rg = blockIdx.y / a.hkv, b = blockIdx.z;
   const int G = a.hq / a.hkv;
   const int wrow0 = rg * (RW * RWW) + rw * RW;
-  const bool wave_live = wrow0 < a.rows;
+  const bool wave_live = !loader && wrow0 < a.rows;
   const int rho = wrow0 + r16;
-  const bool live = rho < a.rows;
+  const bool live = !loader && rho < a.rows;
   const int r = live ? rho / G : 0;
   const int head = g * G + (live ? rho - (rho / G) * G : 0);
   const int32_t* tab = seg_block(a);
@@ -235,16 +239,27 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
   const int64_t tok0_1 = (int64_t)b * a.cap, tok0_2 = (int64_t)b * a.n_new;
 
-  const double fa = a.freq.rev[lane % H];  // wavefront 0: tile angle of frequency `lane`
+  const double fa = a.freq.rev[lane % H];  // loader wavefront 0: tile angle of frequency `lane`
   // Row sources of local tile li (wavefront 0, one row per lane).  The tile
   // flags are double-buffered over 8 tiles: a slow wavefront may still read
   // tile li-1's flag while tile li+3's is being written.
+  // Row sources of local tile li (loader wavefront 0, one row per lane).
+  // The tile flags are double-buffered over 8 tiles: a slow wavefront may
+  // still read tile li-1's flag while tile li+3's is being written.  The
+  // tiles are planned in order, so each lane follows its row's segment
+  // forward from the previous tile instead of searching for it.
+  int s_cur = -1;
   auto plan = [&](int li) {
-    if (wave == 0) {
+    if (wave == NWA) {
       const int u_real = (it0 + li) * kKeyTile + lane;
       const bool real = u_real < T;
       const int u = min(u_real, T - 1);  // rows past the context repeat the last row (masked)
-      const int s = upper_index(seg_start, nseg, u);
+      if (s_cur < 0) {
+        s_cur = upper_index(seg_start, nseg, u);
+      } else {
+        while (s_cur + 1 < nseg && seg_start[s_cur + 1] <= u) ++s_cur;
+      }
+      const int s = s_cur;
       const int64_t tok = seg_src[s] + (u - seg_start[s]);
       const int buf = seg_buf[s];
       // Branch-free select of the source (a pointer select here is otherwise
@@ -276,7 +291,7 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
     const uint16_t* src[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int i = wave + j * NW;  // 0 .. 2*INSTR-1
+      const int i = (wave - NWA) + j * NL;  // 0 .. 2*INSTR-1
       const int mat = i / INSTR, ii = i - mat * INSTR;
       const int off = ii * 1024 + lane * 16;
       const int row = off / Gm::ROW, p = (off % Gm::ROW) >> 4;
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
     // All table reads first, then the loads back to back.
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int i = wave + j * NW;
+      const int i = (wave - NWA) + j * NL;
       const int mat = i / INSTR, ii = i - mat * INSTR;
       dma16(src[j], st + mat * Gm::KBYTES + ii * 1024);
     }
@@ -303,14 +318,14 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
   // counter is reserved for the tile loads).
   double fr[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (tid % CP) + i];
+  for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (ltid % CP) + i];
   float rb_c[KEEP_B ? IPT : 1][8], rb_s[KEEP_B ? IPT : 1][8];
   if constexpr (KEEP_B) {
 #pragma unroll
     for (int k = 0; k < IPT; ++k)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        rope_cs(((tid + k * 64 * NW) / CP) & (kKeyTile - 1), fr[i], rb_c[k][i], rb_s[k][i]);
+        rope_cs(((ltid + k * 64 * NL) / CP) & (kKeyTile - 1), fr[i], rb_c[k][i], rb_s[k][i]);
   }
   const bool writer = rg == 0;  // one row group writes the new tokens back
 
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
     char* st = lds + slot * Gm::STAGE;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-      const int uidx = tid + k * 64 * NW;
+      const int uidx = ltid + k * 64 * NL;
       if (uidx >= kKeyTile * CP) break;
       const int row = uidx / CP, c = uidx - row * CP;
       const uint8_t f = row_flag[slot][row];
@@ -366,25 +381,42 @@ __global__ __launch_bounds__(64 * RWW * KSPL) void k_query_bf16(QueryArgs a) {
     }
   };
 
-  for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
+  // Loader and attention wavefronts run separate loops (so their loop state
+  // can share registers) that meet at the same barriers: one per tile, after
+  // which the loaders request tile li+3 into the stage tile li-1 left and
+  // rotate tile li+1 while the attention wavefronts use tile li.
+  if (loader) {
+    for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
+    waitcnt<0, 0>();
+    barrier_nofence();
+    for (int li = 0; li < NST - 1 && li < cnt; ++li) load(li);
+    if (cnt > 0) {
+      wait_vm<true>(LPW * min(NST - 2, cnt - 1));  // tile 0 landed
+      barrier_nofence();
+      rotate(0);
+    }
+    for (int li = 0; li < cnt; ++li) {
+      if (li + NST - 1 < cnt) plan(li + NST - 1);
+      // Tile li+1 landed (only tile li+2's loads may fly; the rotation's LDS
+      // writes are done too); the barrier publishes tile li's rotation and
+      // the new address table, and frees tile li-1's stage for the refill.
+      wait_vm<true>(LPW * max(0, min(NST - 3, cnt - 2 - li)));
+      barrier_nofence();
+      if (li + NST - 1 < cnt) load(li + NST - 1);
+      if (li + 1 < cnt) rotate(li + 1);
+    }
+    if constexpr (KSPL == 2) {  // the attention wavefronts' merge below
+      __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
   waitcnt<0, 0>();
   barrier_nofence();
-  for (int li = 0; li < NST - 1 && li < cnt; ++li) load(li);
-  if (cnt > 0) {
-    wait_vm<true>(LPW * min(NST - 2, cnt - 1));  // tile 0 landed
-    barrier_nofence();
-    rotate(0);
-  }
+  if (cnt > 0) barrier_nofence();
   for (int li = 0; li < cnt; ++li) {
-    if (li + NST - 1 < cnt) plan(li + NST - 1);
-    // Tile li+1 landed (only tile li+2's loads may fly; LDS writes are done
-    // too); the barrier then publishes tile li's rotation and the new address
-    // table, and frees tile li-1's stage for the refill below.  Tile li+1 is
-    // rotated while tile li is attended: two different stages.
-    wait_vm<true>(LPW * max(0, min(NST - 3, cnt - 2 - li)));
+    waitcnt<0, 0>();  // this wavefront's reads of tile li-1 are done
     barrier_nofence();
-    if (li + NST - 1 < cnt) load(li + NST - 1);
-    if (li + 1 < cnt) rotate(li + 1);
     if (wave_live) {
       const int k0 = (it0 + li) * kKeyTile + kh * KH;
       const int lim = qpos - k0;  // keys kr <= lim are visible (causal over new tokens)
@@ -624,10 +656,10 @@ hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
 template <int D>
 static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
   switch (a.row_waves) {
-    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(128), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(512), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_query_bf16<D, 8, 1>), grid, dim3(512), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(64 * (2 + kQueryLoaders)), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(64 * (4 + kQueryLoaders)), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_query_bf16<D, 8, 1>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
   }
 }
 
