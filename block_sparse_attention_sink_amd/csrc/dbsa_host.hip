@@ -56,6 +56,10 @@ int check_attn(const dbsa_attn_t* a) {
   if (!(a->rope_theta > 0.0) || !std::isfinite(a->rope_theta))
     return fail(DBSA_EINVAL, "rope_theta must be finite and > 0");
   if (!std::isfinite(a->softmax_scale)) return fail(DBSA_EINVAL, "softmax_scale not finite");
+  if (a->rope_inv_freq)
+    for (int i = 0; i < a->head_dim / 2; ++i)
+      if (!(a->rope_inv_freq[i] >= 0.0) || !std::isfinite(a->rope_inv_freq[i]))
+        return fail(DBSA_EINVAL, "rope_inv_freq[%d] must be finite and >= 0", i);
   return DBSA_OK;
 }
 
@@ -104,8 +108,12 @@ int check_ids(const int32_t* ids, int32_t n_ids, int32_t batch, int32_t n_blocks
 RopeFreq make_freq(const dbsa_attn_t* a) {
   RopeFreq f;
   const int half = a->head_dim / 2;
-  for (int i = 0; i < kMaxHalf; ++i)
-    f.rev[i] = i < half ? std::pow(a->rope_theta, -2.0 * i / a->head_dim) / (2.0 * M_PI) : 0.0;
+  for (int i = 0; i < kMaxHalf; ++i) {
+    const double w = i >= half ? 0.0
+                     : a->rope_inv_freq ? a->rope_inv_freq[i]
+                                        : std::pow(a->rope_theta, -2.0 * i / a->head_dim);
+    f.rev[i] = w / (2.0 * M_PI);
+  }
   return f;
 }
 
@@ -528,15 +536,26 @@ size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t
       if (plan_gather(attn, blocks, nullptr, n_ids, batch, nullptr, nullptr, &mb)) return 0;
       return align_up(mb);
     }
+    case DBSA_OP_GATHER_SPANS: {
+      if (check_attn(attn)) return 0;
+      if (batch < 1 || n_ids < 1) {
+        fail(DBSA_EINVAL, "need batch >= 1 and n_spans >= 1");
+        return 0;
+      }
+      const size_t mb = (size_t)batch * (2 * (size_t)n_ids + 1) * sizeof(int32_t);
+      if (check_meta(mb)) return 0;
+      return align_up(mb);
+    }
     case DBSA_OP_QUERY:
-    case DBSA_OP_QUERY_GATHERED: {
+    case DBSA_OP_QUERY_GATHERED:
+    case DBSA_OP_QUERY_SPANS: {
       if (check_attn(attn)) return 0;
       if (batch < 1 || rows < 1 || max_ctx < rows || max_ctx >= (int64_t(1) << 31)) {
         fail(DBSA_EINVAL, "need batch >= 1, n_new >= 1 and n_new <= max_ctx < 2^31");
         return 0;
       }
-      if (op == DBSA_OP_QUERY_GATHERED && n_ids < 1) {
-        fail(DBSA_EINVAL, "n_ids must be >= 1");
+      if (op != DBSA_OP_QUERY && n_ids < 1) {
+        fail(DBSA_EINVAL, "n_ids (n_spans) must be >= 1");
         return 0;
       }
       const int32_t stride = op == DBSA_OP_QUERY ? 3 : n_ids + 3;
@@ -590,26 +609,101 @@ int dbsa_append_block(const dbsa_attn_t* attn, const dbsa_blocks_t* existing, in
   return launch_stage1(attn, existing, p, q_new, p.row0, k_cache, v_cache, o_new, ws, s);
 }
 
-int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const int32_t* ids,
-                     int32_t n_ids, int32_t batch, const void* k_pool, const void* v_pool,
-                     void* k_out, void* v_out, int64_t out_capacity_tokens, int64_t* ctx_len_out,
-                     void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  std::vector<int32_t> tables;
-  std::vector<int64_t> lens;
-  size_t mb = 0;
-  int rc = plan_gather(attn, blocks, ids, n_ids, batch, &tables, &lens, &mb);
-  if (!rc && !ids) rc = fail(DBSA_EINVAL, "ids is NULL");
-  if (!rc) rc = check_ptrs({k_pool, v_pool, k_out, v_out}, "k_pool, v_pool, k_out, v_out");
-  if (!rc && !ctx_len_out) rc = fail(DBSA_EINVAL, "ctx_len_out is NULL");
-  int64_t max_len = 0;
-  if (!rc) {
-    for (int64_t L : lens) max_len = std::max(max_len, L);
-    if (max_len > out_capacity_tokens)
-      rc = fail(DBSA_ENOSPC, "gathered context of %lld tokens exceeds out_capacity_tokens %lld",
-                (long long)max_len, (long long)out_capacity_tokens);
+}  // extern "C"
+
+namespace {
+
+// Pool token spans of each batch row (source token, length), in context
+// order: empty spans dropped, back-to-back spans merged.
+typedef std::vector<std::vector<std::pair<int32_t, int32_t>>> RowSpans;
+
+void add_span(std::vector<std::pair<int32_t, int32_t>>& row, int32_t src, int32_t len) {
+  if (len <= 0) return;
+  if (!row.empty() && row.back().first + row.back().second == src) {
+    row.back().second += len;
+    return;
   }
-  if (!rc) rc = check_ws(ws, ws_bytes, align_up(mb));
+  row.emplace_back(src, len);
+}
+
+// Blocks given by id (anchor first): one span per block.
+RowSpans spans_of_ids(const std::vector<int32_t>& off, const int32_t* ids, int32_t n_ids,
+                      int32_t batch) {
+  RowSpans rs(batch);
+  for (int b = 0; b < batch; ++b)
+    for (int i = 0; i < n_ids; ++i) {
+      const int blkid = ids[(int64_t)b * n_ids + i];
+      add_span(rs[b], off[blkid], off[blkid + 1] - off[blkid]);
+    }
+  return rs;
+}
+
+int check_spans(const int32_t* span_src, const int32_t* span_len, int32_t n_spans, int32_t batch,
+                int64_t pool_tokens, RowSpans& rs) {
+  if (!span_src || !span_len) return fail(DBSA_EINVAL, "span_src or span_len is NULL");
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_spans < 1) return fail(DBSA_EINVAL, "n_spans must be >= 1");
+  if (pool_tokens < 1 || pool_tokens >= (int64_t(1) << 31))
+    return fail(DBSA_EINVAL, "pool_tokens must be in [1, 2^31)");
+  rs.assign(batch, {});
+  for (int b = 0; b < batch; ++b) {
+    int64_t total = 0;
+    for (int i = 0; i < n_spans; ++i) {
+      const int64_t k = (int64_t)b * n_spans + i;
+      const int64_t src = span_src[k], len = span_len[k];
+      if (len < 0 || src < 0 || src + len > pool_tokens)
+        return fail(DBSA_EINVAL, "span [%d][%d] = (%lld, %lld) outside the pool of %lld tokens", b,
+                    i, (long long)src, (long long)len, (long long)pool_tokens);
+      total += len;
+      add_span(rs[b], (int32_t)src, (int32_t)len);
+    }
+    if (total < 1) return fail(DBSA_EINVAL, "batch row %d selects no tokens", b);
+    if (total >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
+  }
+  return DBSA_OK;
+}
+
+size_t max_spans(const RowSpans& rs) {
+  size_t n = 0;
+  for (const auto& r : rs) n = std::max(n, r.size());
+  return n;
+}
+
+// Gather + re-RoPE of pool spans (see RowSpans): row b's spans are written in
+// order at positions 0..T'_b-1.  Tables: start [batch][n + 1] | src [batch][n]
+// with n = the most spans of any row (shorter rows padded with empty spans).
+int gather_spans(const dbsa_attn_t* attn, const RowSpans& rs, int32_t batch, const void* k_pool,
+                 const void* v_pool, void* k_out, void* v_out, int64_t out_capacity_tokens,
+                 int64_t* ctx_len_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_ptrs({k_pool, v_pool, k_out, v_out}, "k_pool, v_pool, k_out, v_out");
+  if (!rc && !ctx_len_out) rc = fail(DBSA_EINVAL, "ctx_len_out is NULL");
+  if (rc) return rc;
+  const int32_t n = (int32_t)max_spans(rs);
+  const size_t mb = (size_t)batch * (2 * n + 1) * sizeof(int32_t);
+  rc = check_meta(mb);
+  if (rc) return rc;
+  std::vector<int32_t> tables((size_t)batch * (2 * n + 1), 0);
+  int32_t* st = tables.data();
+  int32_t* src = st + (size_t)batch * (n + 1);
+  int64_t max_len = 0;
+  std::vector<int64_t> lens(batch, 0);
+  for (int r = 0; r < batch; ++r) {
+    int64_t pos = 0;
+    for (int i = 0; i < n; ++i) {
+      st[(int64_t)r * (n + 1) + i] = (int32_t)pos;
+      if (i < (int)rs[r].size()) {
+        src[(int64_t)r * n + i] = rs[r][i].first;
+        pos += rs[r][i].second;
+      }
+    }
+    st[(int64_t)r * (n + 1) + n] = (int32_t)pos;
+    lens[r] = pos;
+    max_len = std::max(max_len, pos);
+  }
+  if (max_len > out_capacity_tokens)
+    return fail(DBSA_ENOSPC, "gathered context of %lld tokens exceeds out_capacity_tokens %lld",
+                (long long)max_len, (long long)out_capacity_tokens);
+  rc = check_ws(ws, ws_bytes, align_up(mb));
   if (rc) return rc;
   for (int r = 0; r < batch; ++r) ctx_len_out[r] = lens[r];
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -621,8 +715,8 @@ int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const
   ga.k_out = k_out;
   ga.v_out = v_out;
   ga.start = static_cast<const int32_t*>(ws);
-  ga.src = ga.start + (size_t)batch * (n_ids + 1);
-  ga.n_ids = n_ids;
+  ga.src = ga.start + (size_t)batch * (n + 1);
+  ga.n_ids = n;
   ga.hkv = attn->n_kv_heads;
   ga.cap = out_capacity_tokens;
   ga.max_len = (int32_t)max_len;
@@ -630,6 +724,38 @@ int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const
   hipError_t e = launch_gather(ga, batch, attn->head_dim, attn->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "launch gather");
   return DBSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dbsa_gather_rope(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const int32_t* ids,
+                     int32_t n_ids, int32_t batch, const void* k_pool, const void* v_pool,
+                     void* k_out, void* v_out, int64_t out_capacity_tokens, int64_t* ctx_len_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<int32_t> off;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_blocks(blocks, off);
+  if (!rc) rc = check_ids(ids, n_ids, batch, blocks->n_blocks);
+  if (rc) return rc;
+  return gather_spans(attn, spans_of_ids(off, ids, n_ids, batch), batch, k_pool, v_pool, k_out,
+                      v_out, out_capacity_tokens, ctx_len_out, ws, ws_bytes, stream);
+}
+
+int dbsa_gather_rope_spans(const dbsa_attn_t* attn, const int32_t* span_src,
+                           const int32_t* span_len, int32_t n_spans, int32_t batch,
+                           int64_t pool_tokens, const void* k_pool, const void* v_pool,
+                           void* k_out, void* v_out, int64_t out_capacity_tokens,
+                           int64_t* ctx_len_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  RowSpans rs;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_spans(span_src, span_len, n_spans, batch, pool_tokens, rs);
+  if (rc) return rc;
+  return gather_spans(attn, rs, batch, k_pool, v_pool, k_out, v_out, out_capacity_tokens,
+                      ctx_len_out, ws, ws_bytes, stream);
 }
 
 int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const void* q,
@@ -690,6 +816,83 @@ int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const
                            ctx_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Query tokens over pool spans gathered and re-rotated inside the attention's
+// loads, then the row's tail buffer, then (bf16) the new tokens.
+int query_spans(const dbsa_attn_t* attn, const RowSpans& rs, int32_t batch,
+                const void* k_pool, const void* v_pool, int32_t n_new, const void* q,
+                const void* k_new, const void* v_new, void* k_tail, void* v_tail,
+                const int64_t* tail_len, int64_t tail_capacity, void* o, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (n_new == 0) return DBSA_OK;
+  if (!tail_len) return fail(DBSA_EINVAL, "tail_len is NULL");
+  int rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
+                      "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
+  if (rc) return rc;
+  const int32_t n_sp = (int32_t)max_spans(rs);
+  if (n_sp + 2 > kMaxSegments)
+    return fail(DBSA_EUNSUPPORTED,
+                "%d pool spans (after merging back-to-back ones) exceed the %d supported per row",
+                n_sp, kMaxSegments - 2);
+  // Segments: the pool spans (rotated on load), then the row's tail buffer,
+  // then (bf16) the new tokens read from k_new / v_new; float32 appends the
+  // new tokens to the tail buffer first and reads them there.
+  const bool bf16 = attn->dtype == DBSA_BF16;
+  const int32_t stride = n_sp + 3;
+  SegPlan sp;
+  seg_init(sp, batch, stride);
+  int64_t max_ctx = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (tail_len[b] < 0) return fail(DBSA_EINVAL, "tail_len[%d] < 0", b);
+    if (tail_len[b] + n_new > tail_capacity)
+      return fail(DBSA_ENOSPC, "tail_len[%d] + n_new = %lld exceeds tail_capacity %lld", b,
+                  (long long)(tail_len[b] + n_new), (long long)tail_capacity);
+    int32_t* t = sp.tables.data();
+    const size_t row = (size_t)b * stride;
+    const int ns = (int)rs[b].size();
+    int64_t pos = 0;
+    for (int i = 0; i < ns; ++i) {
+      t[sp.o_start + row + i] = (int32_t)pos;
+      t[sp.o_src + row + i] = rs[b][i].first;
+      t[sp.o_buf + row + i] = 0;
+      pos += rs[b][i].second;
+    }
+    const int64_t total = pos + tail_len[b] + n_new;
+    if (total >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
+    t[sp.o_start + row + ns] = (int32_t)pos;  // tail segment
+    t[sp.o_src + row + ns] = 0;
+    t[sp.o_buf + row + ns] = 1;
+    if (bf16) {
+      t[sp.o_start + row + ns + 1] = (int32_t)(pos + tail_len[b]);  // new tokens
+      t[sp.o_src + row + ns + 1] = 0;
+      t[sp.o_buf + row + ns + 1] = 2;
+      t[sp.o_start + row + ns + 2] = (int32_t)total;
+      t[sp.o_nseg + b] = ns + 2;
+    } else {
+      t[sp.o_start + row + ns + 1] = (int32_t)total;
+      t[sp.o_nseg + b] = ns + 1;
+    }
+    t[sp.o_pos0 + b] = (int32_t)(pos + tail_len[b]);
+    t[sp.o_dst + b] = (int32_t)tail_len[b];
+    max_ctx = std::max(max_ctx, total);
+  }
+  QueryPlan qp;
+  query_split(attn, batch, n_new, max_ctx, qp);
+  query_layout(attn, batch, sp.tables.size(), qp);
+  rc = check_meta(qp.meta_bytes);
+  if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
+  if (rc) return rc;
+  return launch_query_path(attn, batch, n_new, q, k_new, v_new, k_pool, v_pool, k_tail, v_tail,
+                           tail_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
 int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
                              const int32_t* ids, int32_t n_ids, int32_t batch,
                              const void* k_pool, const void* v_pool, int32_t n_new,
@@ -706,63 +909,27 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
   rc = check_ids(ids, n_ids, batch, blocks->n_blocks);
   if (rc) return rc;
   if (n_new == 0) return DBSA_OK;
-  if (!tail_len) return fail(DBSA_EINVAL, "tail_len is NULL");
-  rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
-                  "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
+  return query_spans(attn, spans_of_ids(off, ids, n_ids, batch), batch, k_pool, v_pool, n_new, q,
+                     k_new, v_new, k_tail, v_tail, tail_len, tail_capacity, o, ws, ws_bytes,
+                     stream);
+}
+
+int dbsa_query_attn_spans(const dbsa_attn_t* attn, const int32_t* span_src,
+                          const int32_t* span_len, int32_t n_spans, int32_t batch,
+                          int64_t pool_tokens, const void* k_pool, const void* v_pool,
+                          int32_t n_new, const void* q, const void* k_new, const void* v_new,
+                          void* k_tail, void* v_tail, const int64_t* tail_len,
+                          int64_t tail_capacity, void* o, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err[0] = 0;
+  RowSpans rs;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_spans(span_src, span_len, n_spans, batch, pool_tokens, rs);
   if (rc) return rc;
-  if (n_ids + 2 > kMaxSegments)
-    return fail(DBSA_EUNSUPPORTED, "n_ids %d exceeds the %d supported blocks per query", n_ids,
-                kMaxSegments - 2);
-  // Segments: the selected pool blocks (rotated on load), then the row's tail
-  // buffer, then (bf16) the new tokens read from k_new / v_new; float32
-  // appends the new tokens to the tail buffer first and reads them there.
-  const bool bf16 = attn->dtype == DBSA_BF16;
-  const int32_t stride = n_ids + 3;
-  SegPlan sp;
-  seg_init(sp, batch, stride);
-  int64_t max_ctx = 0;
-  for (int b = 0; b < batch; ++b) {
-    if (tail_len[b] < 0) return fail(DBSA_EINVAL, "tail_len[%d] < 0", b);
-    if (tail_len[b] + n_new > tail_capacity)
-      return fail(DBSA_ENOSPC, "tail_len[%d] + n_new = %lld exceeds tail_capacity %lld", b,
-                  (long long)(tail_len[b] + n_new), (long long)tail_capacity);
-    int32_t* t = sp.tables.data();
-    const size_t row = (size_t)b * stride;
-    int64_t pos = 0;
-    for (int i = 0; i < n_ids; ++i) {
-      const int blkid = ids[(int64_t)b * n_ids + i];
-      t[sp.o_start + row + i] = (int32_t)pos;
-      t[sp.o_src + row + i] = off[blkid];
-      t[sp.o_buf + row + i] = 0;
-      pos += off[blkid + 1] - off[blkid];
-    }
-    const int64_t total = pos + tail_len[b] + n_new;
-    if (total >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
-    t[sp.o_start + row + n_ids] = (int32_t)pos;  // tail segment
-    t[sp.o_src + row + n_ids] = 0;
-    t[sp.o_buf + row + n_ids] = 1;
-    if (bf16) {
-      t[sp.o_start + row + n_ids + 1] = (int32_t)(pos + tail_len[b]);  // new tokens
-      t[sp.o_src + row + n_ids + 1] = 0;
-      t[sp.o_buf + row + n_ids + 1] = 2;
-      t[sp.o_start + row + n_ids + 2] = (int32_t)total;
-      t[sp.o_nseg + b] = n_ids + 2;
-    } else {
-      t[sp.o_start + row + n_ids + 1] = (int32_t)total;
-      t[sp.o_nseg + b] = n_ids + 1;
-    }
-    t[sp.o_pos0 + b] = (int32_t)(pos + tail_len[b]);
-    t[sp.o_dst + b] = (int32_t)tail_len[b];
-    max_ctx = std::max(max_ctx, total);
-  }
-  QueryPlan qp;
-  query_split(attn, batch, n_new, max_ctx, qp);
-  query_layout(attn, batch, sp.tables.size(), qp);
-  rc = check_meta(qp.meta_bytes);
-  if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
-  if (rc) return rc;
-  return launch_query_path(attn, batch, n_new, q, k_new, v_new, k_pool, v_pool, k_tail, v_tail,
-                           tail_capacity, o, sp, qp, ws, static_cast<hipStream_t>(stream));
+  if (n_new < 0) return fail(DBSA_EINVAL, "n_new must be >= 0");
+  if (n_new == 0) return DBSA_OK;
+  return query_spans(attn, rs, batch, k_pool, v_pool, n_new, q, k_new, v_new, k_tail, v_tail,
+                     tail_len, tail_capacity, o, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -17,7 +17,7 @@ constexpr int kRowsPerWave = 32;  // query rows per wavefront (MFMA N dimension)
 constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
 constexpr int kPrefillStages = 4;  // LDS stages per K ring and per V ring
-constexpr int kMaxSegments = 512;  // context segments per batch row in Stage 2
+constexpr int kMaxSegments = 1024;  // context segments per batch row in Stage 2
 constexpr int kQueryLoaders = 8;   // Stage-2 wavefronts that plan, load and rotate tiles
 constexpr int kMaxHalf = 64;       // head_dim / 2 upper bound (head_dim <= 128)
 

@@ -16,7 +16,8 @@ import numpy as np
 __all__ = [
     "DbsaError", "load", "dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope",
     "dbsa_query_attn", "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_version",
-    "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "SYMBOLS",
+    "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "OP_GATHER_SPANS",
+    "OP_QUERY_SPANS", "SYMBOLS", "dbsa_gather_rope_spans", "dbsa_query_attn_spans", "llama31_inv_freq",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so")
@@ -24,8 +25,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so"
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 OP_PREFILL, OP_APPEND, OP_GATHER, OP_QUERY, OP_QUERY_GATHERED = 0, 1, 2, 3, 4
+OP_GATHER_SPANS, OP_QUERY_SPANS = 5, 6
 SYMBOLS = ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
-           "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_last_error", "dbsa_version")
+           "dbsa_query_attn_gathered", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
+           "dbsa_workspace_bytes", "dbsa_last_error", "dbsa_version")
 
 
 class DbsaError(RuntimeError):
@@ -37,7 +40,8 @@ class DbsaError(RuntimeError):
 class AttnT(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("rope_inv_freq", ctypes.POINTER(ctypes.c_double))]
 
 
 class BlocksT(ctypes.Structure):
@@ -66,12 +70,16 @@ def load() -> ctypes.CDLL:
     lib.dbsa_query_attn.argtypes = [pa, i32, i32, vp, vp, vp, vp, vp, p64, i64, vp, vp, sz, vp]
     lib.dbsa_query_attn_gathered.argtypes = [pa, pb, p32, i32, i32, vp, vp, i32, vp, vp, vp, vp,
                                              vp, p64, i64, vp, vp, sz, vp]
+    lib.dbsa_gather_rope_spans.argtypes = [pa, p32, p32, i32, i32, i64, vp, vp, vp, vp, i64,
+                                           p64, vp, sz, vp]
+    lib.dbsa_query_attn_spans.argtypes = [pa, p32, p32, i32, i32, i64, vp, vp, i32, vp, vp, vp,
+                                          vp, vp, p64, i64, vp, vp, sz, vp]
     lib.dbsa_workspace_bytes.argtypes = [ctypes.c_int, pa, pb, i64, i32, i32, i64]
     lib.dbsa_workspace_bytes.restype = sz
     lib.dbsa_last_error.restype = ctypes.c_char_p
     lib.dbsa_version.restype = ctypes.c_char_p
     for name in ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
-                 "dbsa_query_attn_gathered"):
+                 "dbsa_query_attn_gathered", "dbsa_gather_rope_spans", "dbsa_query_attn_spans"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -87,8 +95,36 @@ def _check(rc: int):
 
 
 def attn_t(n_q_heads, n_kv_heads, head_dim, dtype, theta, scale=None) -> AttnT:
-    return AttnT(n_q_heads, n_kv_heads, head_dim, dtype, float(theta),
-                 0.0 if scale is None else float(scale))
+    """`theta` is the RoPE base, or an array of head_dim/2 angular frequencies
+    (radians per position) used instead of theta^(-2i/d)."""
+    sc = 0.0 if scale is None else float(scale)
+    if np.ndim(theta) == 0:
+        return AttnT(n_q_heads, n_kv_heads, head_dim, dtype, float(theta), sc, None)
+    w = np.ascontiguousarray(np.asarray(theta, dtype=np.float64).reshape(-1))
+    if w.size != head_dim // 2:
+        raise DbsaError(EINVAL, f"rope frequency table has {w.size} entries, "
+                                f"head_dim / 2 = {head_dim // 2} needed")
+    a = AttnT(n_q_heads, n_kv_heads, head_dim, dtype, 1.0e4, sc,
+              w.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    a._keep = w  # the table must outlive the call
+    return a
+
+
+def llama31_inv_freq(theta: float, head_dim: int, factor: float = 8.0,
+                     low_freq_factor: float = 1.0, high_freq_factor: float = 4.0,
+                     original_context: int = 8192) -> np.ndarray:
+    """Frequency-scaled RoPE table of the Llama-3.1 models (radians per
+    position): frequencies whose wavelength is below original_context /
+    high_freq_factor are kept, those above original_context / low_freq_factor
+    are divided by `factor`, and the band between is blended linearly in
+    original_context / wavelength.  Pass the result as `theta`."""
+    w = theta ** (-(2.0 * np.arange(head_dim // 2, dtype=np.float64)) / head_dim)
+    wavelen = 2.0 * np.pi / w
+    lo_wl = original_context / low_freq_factor
+    hi_wl = original_context / high_freq_factor
+    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    blended = (1.0 - smooth) * w / factor + smooth * w
+    return np.where(wavelen < hi_wl, w, np.where(wavelen > lo_wl, w / factor, blended))
 
 
 class Blocks:
@@ -164,7 +200,7 @@ def dbsa_workspace_bytes(op, n_q_heads, n_kv_heads, head_dim, dtype, theta=1e4, 
     return int(n)
 
 
-def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta: float, scale=None, out=None):
+def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=None):
     """Stage-1 block-sparse prefill of one layer; returns O [N, Hq, d]."""
     import torch
     lib = load()
@@ -311,6 +347,82 @@ def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k
         ctypes.byref(a), ctypes.byref(b.t), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
         n_ids, batch, _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new,
         _ptr(q, "q"), _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+        _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype),
+        tl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(k_tail.shape[1]),
+        _ptr(out, "out", q.dtype), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    return out
+
+
+def _spans(span_src, span_len):
+    src = np.ascontiguousarray(np.atleast_2d(np.asarray(span_src, dtype=np.int32)))
+    ln = np.ascontiguousarray(np.atleast_2d(np.asarray(span_len, dtype=np.int32)))
+    if src.shape != ln.shape:
+        raise DbsaError(EINVAL, f"span_src {src.shape} and span_len {ln.shape} differ")
+    return src, ln
+
+
+def dbsa_gather_rope_spans(k_pool, v_pool, span_src, span_len, theta,
+                           n_q_heads: Optional[int] = None, capacity: Optional[int] = None,
+                           k_out=None, v_out=None):
+    """Gather pool token spans ([batch, n_spans] sources and lengths, in
+    placement order) and re-rotate K at 0..T'-1.  Returns (k_out, v_out,
+    ctx_len) like dbsa_gather_rope."""
+    import torch
+    lib = load()
+    n_pool, hkv, d = k_pool.shape
+    dt = _dtype_code(k_pool)
+    a = attn_t(n_q_heads or hkv, hkv, d, dt, theta)
+    src, ln = _spans(span_src, span_len)
+    batch, n_spans = src.shape
+    if capacity is None:
+        capacity = int(max(1, ln.clip(min=0).sum(axis=1).max()))
+    if k_out is None:
+        k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
+        v_out = torch.empty_like(k_out)
+    ctx = np.zeros(batch, dtype=np.int64)
+    need = lib.dbsa_workspace_bytes(OP_GATHER_SPANS, ctypes.byref(a), None, 0, batch, n_spans, 0)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, k_pool.device)
+    _check(lib.dbsa_gather_rope_spans(
+        ctypes.byref(a), src.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_spans, batch, int(n_pool),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        _ptr(k_out, "k_out", k_pool.dtype), _ptr(v_out, "v_out", k_pool.dtype),
+        int(k_out.shape[1]), ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ws_ptr(ws),
+        _ws_size(ws), _stream(k_pool.device)))
+    return k_out, v_out, ctx
+
+
+def dbsa_query_attn_spans(q, k_new, v_new, k_pool, v_pool, span_src, span_len, k_tail, v_tail,
+                          tail_len: Sequence[int], theta, scale=None, out=None):
+    """Query tokens over pool token spans gathered and re-rotated inside the
+    attention's loads, then the row's tail buffer (see
+    dbsa_query_attn_gathered)."""
+    import torch
+    lib = load()
+    batch, n_new, hq, d = q.shape
+    hkv = k_new.shape[2]
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    src, ln = _spans(span_src, span_len)
+    n_spans = src.shape[1]
+    tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int64).reshape(batch))
+    if out is None:
+        out = torch.empty_like(q)
+    if n_new == 0:
+        return out
+    tp = int(ln.clip(min=0).sum(axis=1).max())
+    need = lib.dbsa_workspace_bytes(OP_QUERY_SPANS, ctypes.byref(a), None, n_new, batch, n_spans,
+                                    tp + int(tl.max()) + n_new)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q.device)
+    _check(lib.dbsa_query_attn_spans(
+        ctypes.byref(a), src.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_spans, batch, int(k_pool.shape[0]),
+        _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new, _ptr(q, "q"),
+        _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
         _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype),
         tl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(k_tail.shape[1]),
         _ptr(out, "out", q.dtype), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))

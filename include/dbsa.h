@@ -62,12 +62,18 @@ enum {
   DBSA_OP_APPEND = 1,
   DBSA_OP_GATHER = 2,
   DBSA_OP_QUERY = 3,
-  DBSA_OP_QUERY_GATHERED = 4
+  DBSA_OP_QUERY_GATHERED = 4,
+  DBSA_OP_GATHER_SPANS = 5,
+  DBSA_OP_QUERY_SPANS = 6
 };
 
 /* Shape of one attention layer.
  * n_q_heads % n_kv_heads == 0; head_dim in {64, 128}; dtype DBSA_BF16 or
- * DBSA_F32; rope_theta > 0; softmax_scale <= 0 selects 1/sqrt(head_dim). */
+ * DBSA_F32; rope_theta > 0; softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * rope_inv_freq: NULL for the plain frequencies theta^(-2i/d), or a host
+ * double[head_dim / 2] of angular frequencies (radians per position, finite,
+ * >= 0) replacing them, e.g. a frequency-scaled table for long contexts (the
+ * method's pages give only theta); read before the call returns. */
 typedef struct {
   int32_t n_q_heads;
   int32_t n_kv_heads;
@@ -75,6 +81,7 @@ typedef struct {
   int32_t dtype;
   double rope_theta;
   float softmax_scale;
+  const double* rope_inv_freq;
 } dbsa_attn_t;
 
 /* The demonstration pool cut into blocks [Notes, Method > Stage 1, item 1].
@@ -165,13 +172,41 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
                              int64_t tail_capacity, void* o,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Stage 2 at example granularity [Notes, Ablations > block-level vs
+ * example-level retrieval]: the context is a list of pool token spans (for
+ * instance single demonstrations) instead of whole blocks.
+ *   span_src, span_len: host int32[batch][n_spans]: first pool token and length
+ *   of each span, in the order the spans are placed (positions 0, 1, ... over
+ *   their concatenation).  Lengths may be 0 (skipped); every span must lie in
+ *   [0, pool_tokens); a row must select at least one token.  The anchor is not
+ *   implied: the caller lists the spans it wants, the anchor's first.  Spans
+ *   that continue each other in the pool are merged; at most 1022 spans per
+ *   row may remain (DBSA_EUNSUPPORTED otherwise).
+ * dbsa_gather_rope_spans: as dbsa_gather_rope with spans for blocks.
+ * dbsa_query_attn_spans: as dbsa_query_attn_gathered with spans for blocks. */
+int dbsa_gather_rope_spans(const dbsa_attn_t* attn, const int32_t* span_src,
+                           const int32_t* span_len, int32_t n_spans, int32_t batch,
+                           int64_t pool_tokens, const void* k_pool, const void* v_pool,
+                           void* k_out, void* v_out, int64_t out_capacity_tokens,
+                           int64_t* ctx_len_out, void* ws, size_t ws_bytes, void* stream);
+int dbsa_query_attn_spans(const dbsa_attn_t* attn, const int32_t* span_src,
+                          const int32_t* span_len, int32_t n_spans, int32_t batch,
+                          int64_t pool_tokens, const void* k_pool, const void* v_pool,
+                          int32_t n_new, const void* q, const void* k_new, const void* v_new,
+                          void* k_tail, void* v_tail, const int64_t* tail_len,
+                          int64_t tail_capacity, void* o,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes the operation needs.
  *   op: DBSA_OP_*.  blocks: the pool (for DBSA_OP_APPEND, the existing pool).
- *   rows: PREFILL ignores it; APPEND: new_len; QUERY / QUERY_GATHERED: n_new;
- *   GATHER: ignored.  batch: Stage-2 batch (ignored for Stage 1).
- *   n_ids: ids per row (GATHER, QUERY_GATHERED), else ignored.
+ *   rows: PREFILL ignores it; APPEND: new_len; QUERY / QUERY_GATHERED /
+ *   QUERY_SPANS: n_new; GATHER, GATHER_SPANS: ignored.  batch: Stage-2 batch
+ *   (ignored for Stage 1).  n_ids: ids per row (GATHER, QUERY_GATHERED) or
+ *   n_spans (GATHER_SPANS, QUERY_SPANS), else ignored.  blocks: ignored by
+ *   the span operations (may be NULL).
  *   max_ctx: QUERY: the largest ctx_len[b] + n_new the call will see;
- *   QUERY_GATHERED: the largest T'_b + tail_len[b] + n_new; else ignored.
+ *   QUERY_GATHERED / QUERY_SPANS: the largest T'_b + tail_len[b] + n_new;
+ *   else ignored.
  * Returns 0 and sets the error text on invalid arguments. */
 size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
                             int64_t rows, int32_t batch, int32_t n_ids, int64_t max_ctx);

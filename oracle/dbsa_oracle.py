@@ -14,7 +14,8 @@ Readings taken where the page is silent (each one is listed in the design
 document):
   * positions are token positions; block lengths are given in tokens;
   * RoPE is the rotate-half form: pair (i, i + d/2) is rotated by p * w_i with
-    w_i = theta ** (-2 i / d), no frequency scaling;
+    w_i = theta ** (-2 i / d), no frequency scaling (a caller may pass its own
+    w_i table instead of theta);
   * the sink is the whole first block; previous blocks and the sink are seen in
     full, the own block causally (diagonal included);
   * softmax scale is 1/sqrt(d) unless given; GQA maps q head h to kv head
@@ -38,6 +39,7 @@ __all__ = [
     "prefill",
     "append_block",
     "gather_rope",
+    "gather_rope_spans",
     "query_attn",
     "decode",
 ]
@@ -61,7 +63,7 @@ def token_block(block_lens) -> np.ndarray:
     return np.repeat(np.arange(lens.size, dtype=np.int64), lens)
 
 
-def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
+def rope(x: np.ndarray, pos, theta) -> np.ndarray:
     """Rotary position transform of x [T, H, d] at integer positions pos [T].
 
     [Notes, Method > Stage 1, item 3] (sequential positions, K/V kept before the
@@ -70,11 +72,16 @@ def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
     i < d/2, w_i = theta^(-2i/d), phi = p * w_i (float64) and
         (x_i, x_{i+d/2}) -> (x_i cos phi - x_{i+d/2} sin phi,
                              x_{i+d/2} cos phi + x_i sin phi).
+    `theta` may instead be the d/2 angular frequencies w_i themselves (radians
+    per position), for frequency-scaled variants the page leaves open.
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     half = d // 2
-    w = float(theta) ** (-(2.0 * np.arange(half, dtype=np.float64)) / d)
+    if np.ndim(theta) == 0:
+        w = float(theta) ** (-(2.0 * np.arange(half, dtype=np.float64)) / d)
+    else:
+        w = np.asarray(theta, dtype=np.float64).reshape(half)
     phi = np.asarray(pos, dtype=np.float64)[:, None] * w[None, :]  # [T, d/2]
     c = np.cos(phi)[:, None, :]
     s = np.sin(phi)[:, None, :]
@@ -191,6 +198,19 @@ def gather_rope(k_pool, v_pool, block_lens, ids, theta: float):
     ids = [int(b) for b in ids]
     k_sel = np.concatenate([np.asarray(k_pool, np.float64)[off[b]:off[b + 1]] for b in ids])
     v_sel = np.concatenate([np.asarray(v_pool, np.float64)[off[b]:off[b + 1]] for b in ids])
+    return rope(k_sel, np.arange(k_sel.shape[0]), theta), v_sel
+
+
+def gather_rope_spans(k_pool, v_pool, span_src, span_len, theta):
+    """Stage-2 KV assembly at example granularity, [Notes, Ablations >
+    block-level vs example-level retrieval]: the cached K/V of the pool token
+    spans [src, src + len), in the given order, concatenated; K rotated at the
+    new sequential positions 0..T'-1, V not rotated."""
+    k_pool = np.asarray(k_pool, np.float64)
+    v_pool = np.asarray(v_pool, np.float64)
+    idx = np.concatenate([np.arange(int(s), int(s) + int(n), dtype=np.int64)
+                          for s, n in zip(span_src, span_len)])
+    k_sel, v_sel = k_pool[idx], v_pool[idx]
     return rope(k_sel, np.arange(k_sel.shape[0]), theta), v_sel
 
 

@@ -4,6 +4,8 @@ call (with the documented status codes)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -26,6 +28,19 @@ def test_exports_every_declared_symbol(lib):
     for name in declared:
         assert hasattr(lib, name), name
     assert "gfx950" in dbsa.dbsa_version()
+
+
+def test_exports_nothing_else_with_c_linkage():
+    """Host helpers stay internal: the only unmangled functions the library
+    exports are the declared entry points."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", dbsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    plain = {ln.split()[-1] for ln in out.splitlines()
+             if ln.split()[1:2] == ["T"] and not ln.split()[-1].startswith("_Z")}
+    assert plain == set(dbsa.SYMBOLS)
 
 
 def _attn(hq=4, hkv=2, d=128, dt=dbsa.BF16, theta=1e4):
@@ -61,6 +76,32 @@ def test_prefill_validation(lib):
     assert "workspace too small" in _err(lib)
     big = dbsa.Blocks(np.full(3, 1 << 30, np.int32), 1, 2)
     assert _prefill(lib, _attn(), big) == dbsa.EINVAL
+
+
+def test_rope_table_validation_and_llama31_helper(lib):
+    ok_blocks = dbsa.Blocks([5, 7, 9], 1, 2)
+    table = dbsa.llama31_inv_freq(5e5, 128)
+    # a valid table passes the argument checks (the launch itself needs a GPU)
+    assert _prefill(lib, dbsa.attn_t(4, 2, 128, dbsa.BF16, table), ok_blocks) not in (
+        dbsa.EINVAL, dbsa.EUNSUPPORTED)
+    for bad in (np.nan, -1.0, np.inf):
+        t = table.copy()
+        t[7] = bad
+        assert _prefill(lib, dbsa.attn_t(4, 2, 128, dbsa.BF16, t), ok_blocks) == dbsa.EINVAL
+        assert "rope_inv_freq[7]" in _err(lib)
+    with pytest.raises(dbsa.DbsaError):
+        dbsa.attn_t(4, 2, 128, dbsa.BF16, table[:10])
+    # Helper properties: high frequencies (wavelength < 8192 / 4) unchanged, low
+    # ones (wavelength > 8192) divided by 8, the band between monotone and
+    # continuous with both ends.
+    plain = 5e5 ** (-(2.0 * np.arange(64)) / 128)
+    wl = 2 * np.pi / plain
+    hi, lo = wl < 2048, wl > 8192
+    np.testing.assert_array_equal(table[hi], plain[hi])
+    np.testing.assert_allclose(table[lo], plain[lo] / 8, rtol=1e-15)
+    assert np.all(np.diff(table) < 0)
+    mid = ~hi & ~lo
+    assert np.all(table[mid] <= plain[mid]) and np.all(table[mid] >= plain[mid] / 8)
 
 
 def _gather(lib, ids, n_blocks=6, cap=1 << 20, ws_bytes=1 << 30, ctx=True):
@@ -153,3 +194,55 @@ def test_workspace_sizes(lib):
     q = dbsa.dbsa_workspace_bytes(dbsa.OP_QUERY, 32, 8, 128, dbsa.BF16, rows=64, batch=1,
                                   max_ctx=28000)
     assert q > 0
+
+
+def _span_call(lib, fn, src, ln, pool=100, cap=1 << 20, n_new=4, tail_cap=1 << 20):
+    src = np.ascontiguousarray(np.atleast_2d(np.asarray(src, np.int32)))
+    ln = np.ascontiguousarray(np.atleast_2d(np.asarray(ln, np.int32)))
+    p32 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    batch, n = src.shape
+    a = _attn()
+    out = np.zeros(batch, np.int64)
+    if fn == "gather":
+        return lib.dbsa_gather_rope_spans(ctypes.byref(a), p32(src), p32(ln), n, batch, pool,
+                                          FAKE, FAKE, FAKE, FAKE, cap,
+                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                          FAKE, 1 << 40, None)
+    return lib.dbsa_query_attn_spans(ctypes.byref(a), p32(src), p32(ln), n, batch, pool, FAKE,
+                                     FAKE, n_new, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), tail_cap,
+                                     FAKE, FAKE, 1 << 40, None)
+
+
+@pytest.mark.parametrize("fn", ["gather", "query"])
+def test_span_validation(lib, fn):
+    assert _span_call(lib, fn, [[0, 95]], [[10, 6]]) == dbsa.EINVAL  # past the pool
+    assert "outside the pool" in _err(lib)
+    assert _span_call(lib, fn, [[-1, 5]], [[2, 3]]) == dbsa.EINVAL
+    assert _span_call(lib, fn, [[0, 5]], [[2, -3]]) == dbsa.EINVAL
+    assert _span_call(lib, fn, [[0, 5], [3, 4]], [[2, 3], [0, 0]]) == dbsa.EINVAL
+    assert "selects no tokens" in _err(lib)
+    assert _span_call(lib, fn, [[0, 5]], [[2, 3]], pool=0) == dbsa.EINVAL
+    a = _attn()
+    p = np.zeros((1, 2), np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if fn == "gather":
+        assert lib.dbsa_gather_rope_spans(ctypes.byref(a), None, p, 2, 1, 100, FAKE, FAKE, FAKE,
+                                          FAKE, 100, None, FAKE, 1 << 40, None) == dbsa.EINVAL
+        assert _span_call(lib, fn, [[0, 50]], [[20, 20]], cap=39) == dbsa.ENOSPC
+    else:
+        assert lib.dbsa_query_attn_spans(ctypes.byref(a), p, None, 2, 1, 100, FAKE, FAKE, 4,
+                                         FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, FAKE, FAKE,
+                                         1 << 40, None) == dbsa.EINVAL
+        assert _span_call(lib, fn, [[0, 5]], [[2, 3]], n_new=-1) == dbsa.EINVAL
+        assert _span_call(lib, fn, [[0, 5]], [[2, 3]], n_new=0) == dbsa.OK  # nothing enqueued
+        assert _span_call(lib, fn, [[0, 5]], [[2, 3]], tail_cap=3) == dbsa.ENOSPC
+        # Back-to-back spans merge into one segment; 1100 separated spans
+        # exceed the per-row segment table, 1100 adjacent ones do not.
+        n = 1100
+        gaps = np.arange(n, dtype=np.int32) * 2
+        assert _span_call(lib, fn, [gaps], [np.ones(n, np.int32)], pool=4 * n) == \
+            dbsa.EUNSUPPORTED
+        assert "exceed" in _err(lib)
+        adj = np.arange(n, dtype=np.int32)
+        assert _span_call(lib, fn, [adj], [np.ones(n, np.int32)], pool=4 * n) not in (
+            dbsa.EINVAL, dbsa.EUNSUPPORTED)

@@ -251,6 +251,20 @@ def test_query_fused_equals_materialised_bitwise():
     assert torch.equal(a, b)
 
 
+def test_rope_frequency_table_prefill_and_stage2():
+    """A frequency-scaled RoPE table (Llama-3.1 style) through prefill and both
+    Stage-2 paths, against the oracle given the same table."""
+    table = dbsa.llama31_inv_freq(5e5, 128)
+    rng = np.random.default_rng(29)
+    lens = rng.integers(40, 500, size=7).astype(np.int32)
+    got, want = _run_prefill(lens, 8, 2, 128, "bf16", 1, 2, table, seed=151)
+    assert_close(got, want, "bf16", "prefill with table")
+    ids = np.array([[0, 3, 6, 2]], np.int32)
+    a = _stage2_case("bf16", 8, 2, 128, lens, ids, 17, table, 161, False)
+    b = _stage2_case("bf16", 8, 2, 128, lens, ids, 17, table, 161, True)
+    assert torch.equal(a, b)
+
+
 def test_anchor_only_and_single_token():
     lens = np.array([70, 33, 90], np.int32)
     _stage2_case("bf16", 4, 4, 128, lens, np.array([[0]], np.int32), 1, 1e4, 131, False)
@@ -318,3 +332,77 @@ def test_batched_queries_own_ids():
                     for _ in range(6)]).astype(np.int32)
     for fused in (False, True):
         _stage2_case("bf16", 8, 2, 128, lens, ids, 5, 5e5, 161, fused)
+
+
+def _span_case(dtype, hq, hkv, d, n_pool, src, ln, n_new, theta, seed):
+    """Example-level retrieval: gather pool token spans (fused and via the
+    materialised gather) and run the query over them; both against the oracle."""
+    kp = randn((n_pool, hkv, d), seed, dtype, DEV)
+    vp = randn((n_pool, hkv, d), seed + 1, dtype, DEV)
+    batch = src.shape[0]
+    q = randn((batch, n_new, hq, d), seed + 5, dtype, DEV)
+    kn = randn((batch, n_new, hkv, d), seed + 6, dtype, DEV)
+    vn = randn((batch, n_new, hkv, d), seed + 7, dtype, DEV)
+    tp = int(ln.sum(axis=1).max())
+    ko, vo, ctx = dbsa.dbsa_gather_rope_spans(kp, vp, src, ln, theta, n_q_heads=hq,
+                                              capacity=tp + n_new)
+    o_mat = dbsa.dbsa_query_attn(q, kn, vn, ko, vo, ctx, theta)
+    tail_k = torch.zeros((batch, n_new, hkv, d), dtype=TORCH_DT[dtype], device=DEV)
+    tail_v = torch.zeros_like(tail_k)
+    o_fused = dbsa.dbsa_query_attn_spans(q, kn, vn, kp, vp, src, ln, tail_k, tail_v, [0] * batch,
+                                         theta)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        kg, vg = orc.gather_rope_spans(host64(kp), host64(vp), src[b], ln[b], theta)
+        assert ctx[b] == kg.shape[0]
+        np.testing.assert_array_equal(host64(vo[b, :ctx[b]]), vg)
+        if dtype == "bf16":
+            assert_bf16_rounding(host64(ko[b, :ctx[b]]), kg, f"span gather K row {b}")
+        else:
+            assert_close(host64(ko[b, :ctx[b]]), kg, "f32", f"span gather K row {b}")
+        want, _, _ = orc.query_attn(host64(q[b]), host64(kn[b]), host64(vn[b]), kg, vg, theta)
+        assert_close(host64(o_mat[b]), want, dtype, f"span query b={b} materialised")
+        assert_close(host64(o_fused[b]), want, dtype, f"span query b={b} fused")
+    return o_mat, o_fused
+
+
+def _demo_spans(rng, n_pool, anchor, rows, n_demos, lo, hi):
+    """Anchor span first, then demonstrations at arbitrary pool offsets (not
+    block-aligned); some rows get fewer demos (zero-length padding), one pair
+    of demos is back to back."""
+    src = np.zeros((rows, n_demos + 1), np.int32)
+    ln = np.zeros((rows, n_demos + 1), np.int32)
+    for r in range(rows):
+        src[r, 0], ln[r, 0] = 0, anchor
+        k = n_demos - (r % 3)
+        for i in range(1, k + 1):
+            ln[r, i] = rng.integers(lo, hi)
+            src[r, i] = rng.integers(anchor, n_pool - ln[r, i])
+        if k >= 3:
+            src[r, 3] = src[r, 2] + ln[r, 2]
+            ln[r, 3] = min(ln[r, 3], n_pool - src[r, 3])
+    return src, ln
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_example_level_spans(dtype):
+    rng = np.random.default_rng(37)
+    n_pool = 4000
+    src, ln = _demo_spans(rng, n_pool, 57, 3, 9, 5, 120)
+    hq, hkv, d = (8, 2, 128) if dtype == "bf16" else (2, 1, 64)
+    o_mat, o_fused = _span_case(dtype, hq, hkv, d, n_pool, src, ln, 13, 1e4, 171)
+    if dtype == "bf16":
+        assert torch.equal(o_mat, o_fused)
+
+
+def test_example_level_many_short_spans():
+    """Hundreds of one- to three-token spans per row: many segments per tile,
+    a segment change inside almost every key tile."""
+    rng = np.random.default_rng(41)
+    n_pool = 3000
+    n = 700
+    src = np.stack([np.sort(rng.choice(n_pool - 3, n, replace=False)) for _ in range(2)])
+    ln = rng.integers(1, 4, size=(2, n))
+    src, ln = src.astype(np.int32), ln.astype(np.int32)
+    o_mat, o_fused = _span_case("bf16", 8, 2, 128, n_pool, src, ln, 6, 5e5, 181)
+    assert torch.equal(o_mat, o_fused)

@@ -66,6 +66,35 @@ def test_rope_identity_norm_and_relativity():
     np.testing.assert_allclose(r1, r2, atol=1e-12)
 
 
+def test_rope_frequency_table_is_pairwise_rotation():
+    """A caller's frequency table: each pair (i, i + d/2) turns by p * w_i.
+
+    Checked against 2x2 rotation matrices applied pair by pair in a loop, and
+    the table theta^(-2i/d) reproduces the theta form exactly.
+    """
+    rng = _rng(21)
+    d = 16
+    w = np.abs(rng.standard_normal(d // 2)) * 0.3
+    x = rng.standard_normal((4, 2, d))
+    pos = np.array([0, 3, 250, 77777])
+    want = np.empty_like(x)
+    for t, p in enumerate(pos):
+        for i in range(d // 2):
+            c, s = np.cos(p * w[i]), np.sin(p * w[i])
+            rot = np.array([[c, -s], [s, c]])
+            pair = np.stack([x[t, :, i], x[t, :, i + d // 2]])  # [2, H]
+            out = rot @ pair
+            want[t, :, i], want[t, :, i + d // 2] = out[0], out[1]
+    np.testing.assert_allclose(orc.rope(x, pos, w), want, atol=1e-12)
+    plain = 5e5 ** (-(2.0 * np.arange(d // 2)) / d)
+    np.testing.assert_array_equal(orc.rope(x, pos, plain), orc.rope(x, pos, 5e5))
+    # relativity holds for any table
+    q, k = rng.standard_normal((1, 1, d)), rng.standard_normal((1, 1, d))
+    lhs = np.sum(orc.rope(q, [9000], w) * orc.rope(k, [1234], w))
+    rhs = np.sum(orc.rope(q, [9000 - 1234], w) * k)
+    assert abs(lhs - rhs) < 1e-9
+
+
 # ----------------------------------------------------------------------------
 # Mask: two formulations and the closed form of the row counts
 # ----------------------------------------------------------------------------
@@ -315,6 +344,38 @@ def test_gather_places_blocks_in_given_order():
     np.testing.assert_array_equal(vg, raw_v)
     # Undo the rotation with the inverse (negative) positions: recovers the cache.
     np.testing.assert_allclose(orc.rope(kg, -np.arange(kg.shape[0]), 1e4), raw_k, atol=1e-13)
+
+
+def test_gather_spans_places_tokens_in_given_order():
+    """Example-level spans: token t of the result is the pool token at the
+    t-th place of the spans' concatenation, K turned back by -t recovers it,
+    and spans that cover whole blocks give the block gather exactly."""
+    rng = _rng(12)
+    lens = [3, 5, 2, 4]
+    n = sum(lens)
+    k = rng.standard_normal((n, 2, 8))
+    v = rng.standard_normal((n, 2, 8))
+    src, ln = [0, 11, 4, 1, 9], [2, 3, 0, 3, 1]
+    kg, vg = orc.gather_rope_spans(k, v, src, ln, 1e4)
+    order = []
+    for s_, l_ in zip(src, ln):
+        t = s_
+        while t < s_ + l_:
+            order.append(t)
+            t += 1
+    assert order == [0, 1, 11, 12, 13, 1, 2, 3, 9]
+    assert kg.shape[0] == len(order)
+    for t, p in enumerate(order):
+        np.testing.assert_array_equal(vg[t], v[p])
+        np.testing.assert_allclose(orc.rope(kg[t:t + 1], [-t], 1e4)[0], k[p], atol=1e-13)
+    kb, vb = orc.gather_rope(k, v, lens, [0, 3, 1], 1e4)
+    ks, vs = orc.gather_rope_spans(k, v, [0, 10, 3], [3, 4, 5], 1e4)
+    np.testing.assert_array_equal(ks, kb)
+    np.testing.assert_array_equal(vs, vb)
+    # splitting a span in two changes nothing
+    k2, v2 = orc.gather_rope_spans(k, v, [0, 10, 12, 3], [3, 2, 2, 5], 1e4)
+    np.testing.assert_array_equal(k2, kb)
+    np.testing.assert_array_equal(v2, vb)
 
 
 def test_anchor_only_stage2_is_causal_sdpa_over_anchor_and_query():
