@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "dbsa_internal.hpp"
 
 namespace dbsa {
@@ -207,6 +210,17 @@ constexpr float kLazy = 8.0f;
 // if-converting the body into selects that every tile would then execute (the
 // element mask of partly visible tiles and the softmax reference raise).
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop
+// whose index is a compile-time constant in the body (register-array index).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedTrans = 0x400;

@@ -11,11 +11,13 @@
 //   k_new_kv_f32                   rotate the new tokens' K at their positions
 //                                  and append K/V to the row's context buffer
 //                                  (float32 path; bf16 does it in k_query_bf16).
-//   k_query_bf16<D, RWW, KSPL>     split-K flash attention of the packed
+//   k_query_bf16<D, RWW, KSPL>     split-K flash attention of up to 64 packed
 //                                  (token, head-in-group) rows of one KV head
 //                                  over a segment list (pool blocks and new
 //                                  tokens are rotated while staged; new tokens
 //                                  are also appended to the context buffer).
+//   k_query_wide_bf16<D, NWA>      the same for more rows: 32-row wavefronts
+//                                  on the software-pipelined prefill core.
 //   k_combine                      log-sum-exp merge of the split partials.
 //   k_query_f32                    float32 rows (one wavefront per row).
 #include "dbsa_device.hpp"
@@ -137,48 +139,126 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row sources of the 64-key tiles of one split (one row per lane of the
+// planning wavefront): address of the row's K and V (pool, context buffer or
+// new tokens), whether it is rotated (pool rows and new tokens) and whether
+// it is a new token (also written to the context buffer), plus the tile's
+// RoPE angles cos / sin(w_i u0).  Tiles are planned in order, so each lane
+// follows its row's segment forward instead of searching for it; tiles past
+// the context repeat its last row (masked), so their loads stay in bounds.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+struct TilePlanner {
+  static constexpr uint8_t kRot = 1, kNew = 2;
+  uint64_t kb0, vb0, kb1, vb1, kb2, vb2;
+  int64_t tok0_1, tok0_2;
+  int hkv, g, T, nseg, dst0, it0, s_cur;
+  double fa;
+
+  __device__ __forceinline__ TilePlanner(const QueryArgs& a, int b, int g_, int T_, int nseg_,
+                                         int dst0_,
+                         int it0_, int lane)
+      : kb0(reinterpret_cast<uint64_t>(a.k_pool)), vb0(reinterpret_cast<uint64_t>(a.v_pool)),
+        kb1(reinterpret_cast<uint64_t>(a.k_ctx)), vb1(reinterpret_cast<uint64_t>(a.v_ctx)),
+        kb2(reinterpret_cast<uint64_t>(a.k_new)), vb2(reinterpret_cast<uint64_t>(a.v_new)),
+        tok0_1((int64_t)b * a.cap), tok0_2((int64_t)b * a.n_new), hkv(a.hkv), g(g_), T(T_),
+        nseg(nseg_), dst0(dst0_), it0(it0_), s_cur(-1), fa(a.freq.rev[lane % (D / 2)]) {}
+
+  __device__ __forceinline__ void plan(int li, int lane, const int32_t* seg_start,
+                                       const int32_t* seg_src, const int32_t* seg_buf,
+                                       uint64_t (*row_k)[kKeyTile], uint64_t (*row_v)[kKeyTile],
+                                       uint8_t (*row_flag)[kKeyTile], int32_t (*row_dst)[kKeyTile],
+                                       f32x2 (*rot_a)[kMaxHalf]) {
+    const int u_real = (it0 + li) * kKeyTile + lane;
+    const bool real = u_real < T;
+    const int u = min(u_real, T - 1);
+    if (s_cur < 0) {
+      s_cur = upper_index(seg_start, nseg, u);
+    } else {
+      while (s_cur + 1 < nseg && seg_start[s_cur + 1] <= u) ++s_cur;
+    }
+    const int sg = s_cur;
+    const int64_t tok = seg_src[sg] + (u - seg_start[sg]);
+    const int buf = seg_buf[sg];
+    // Branch-free select of the source (a pointer select here is otherwise
+    // lowered to a lookup table in scratch memory).
+    const uint64_t m0 = buf == 0 ? ~0ull : 0ull, m1 = buf == 1 ? ~0ull : 0ull;
+    const uint64_t m2 = ~(m0 | m1);
+    const int64_t trow = (buf == 0 ? 0 : buf == 1 ? tok0_1 : tok0_2) + tok;
+    const uint64_t off = 2ull * static_cast<uint64_t>((trow * hkv + g) * D);
+    const int slot = li & (NT - 1);
+    row_k[slot][lane] = ((kb0 & m0) | (kb1 & m1) | (kb2 & m2)) + off;
+    row_v[slot][lane] = ((vb0 & m0) | (vb1 & m1) | (vb2 & m2)) + off;
+    row_flag[slot][lane] = real ? (buf != 1 ? kRot : 0) | (buf == 2 ? kNew : 0) : 0;
+    row_dst[slot][lane] = dst0 + (int)tok;
+    if (lane < D / 2) {
+      float c, sn;
+      rope_cs((int64_t)(it0 + li) * kKeyTile, fa, c, sn);
+      rot_a[slot][lane] = f32x2{c, sn};
+    }
+  }
+};
+
+// Rotate one (row, chunk pair) of a K tile at u0 + row: angle(u0 + row) =
+// angle(u0) (tile table ap: cos, sin of 8 frequencies) + angle(row) (row
+// table bp), two frequencies (one 32-bit word of each chunk) at a time.
+__device__ __forceinline__ void rotate_pair(u32x4& x1, u32x4& x2, const f32x4* ap,
+                                            const f32x4* bp) {
+  uint32_t wa[4] = {x1.x, x1.y, x1.z, x1.w}, wb[4] = {x2.x, x2.y, x2.z, x2.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    // Half the angle reads at a time (fewer registers than all eight).
+    if (h == 2) __builtin_amdgcn_sched_barrier(0);
+    const f32x4 av = ap[h], bv = bp[h];
+    float c0, s0, c1, s1;
+    angle_add(av[0], av[1], bv[0], bv[1], c0, s0);
+    angle_add(av[2], av[3], bv[2], bv[3], c1, s1);
+    const float a0 = bf16_lo(wa[h]), a1 = bf16_hi(wa[h]);
+    const float b0 = bf16_lo(wb[h]), b1 = bf16_hi(wb[h]);
+    wa[h] = pack_bf16x2(rot_lo(a0, b0, c0, s0), rot_lo(a1, b1, c1, s1));
+    wb[h] = pack_bf16x2(rot_hi(a0, b0, c0, s0), rot_hi(a1, b1, c1, s1));
+  }
+  x1 = u32x4{wa[0], wa[1], wa[2], wa[3]};
+  x2 = u32x4{wb[0], wb[1], wb[2], wb[3]};
+}
+
+// ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
-// Workgroup = RWW x KSPL wavefronts over 16 RWW packed rows (row = token * G +
-// head in group) of one KV head and one key split: 16 rows per wavefront on
-// v_mfma_f32_16x16x32_bf16 (see Flash16), and with KSPL = 2 the two halves of
-// every 64-key tile go to two wavefronts with their own softmax state, merged
-// through LDS at the end (twice the wavefronts per SIMD to hide the latency
-// of one tile's dependent MFMA / shuffle / LDS chain).  Each tile is staged by
-// direct global->LDS loads through a ring of 4 stages, three tiles ahead:
-// per tile, wavefront 0 first resolves every row's source (segment lookup in
-// LDS) into a small address table, then all wavefronts issue the loads.
-// Rows from the pool or from the new tokens arrive unrotated and are rotated
-// in LDS at their virtual position before the tile is used; the first row
-// group also writes the new tokens' rotated K and their V to the context
-// buffer (each new token lies in exactly one tile of one split).
+// Workgroup = RWW x KSPL attention wavefronts over 16 RWW packed rows (row =
+// token * G + head in group) of one KV head and one key split, plus
+// kQueryLoaders loader wavefronts.  Attention: 16 rows per wavefront on
+// v_mfma_f32_16x16x32_bf16 (see Flash16); with KSPL = 2 the two halves of
+// every 64-key tile go to two wavefronts with their own softmax state,
+// merged through LDS at the end.  Loaders: each thread owns one (row, chunk
+// pair) of every tile; it loads the pair's K and V bytes into registers
+// kLead tiles ahead of use, rotates K at the row's virtual position in
+// registers, and writes both into a two-stage LDS ring (row sources come
+// from a per-tile address table that loader wavefront 0 plans one tile
+// before the loads).  The loads' completion is tracked by the compiler, so
+// each rotation waits for exactly its own tile.  Rows of the new tokens also
+// go to the context buffer (the first row group writes them).
 // ---------------------------------------------------------------------------
 template <int D, int RWW, int KSPL>
 __global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
-  // RWW x KSPL attention wavefronts, then NL loader wavefronts that plan,
-  // load and rotate the tiles ahead of the attention.
   constexpr int NWA = RWW * KSPL, NL = kQueryLoaders, NW = NWA + NL, KH = kKeyTile / KSPL;
   constexpr int KS = D / 32, OT = D / 16, CP = D / 16, CR = D / 8;
-  constexpr int RW = 16;  // rows per wavefront
-  constexpr int NST = 4;
-  constexpr int INSTR = Gm::TU4 / 64;  // 1 KiB loads per matrix per tile
-  constexpr int LPW = 2 * INSTR / NL;  // loads per loader wave per tile
-  static_assert((2 * INSTR) % NL == 0, "loads must split evenly over the loader waves");
-  static_assert((64 * NL) % CP == 0, "each loader thread keeps one chunk pair");
+  constexpr int RW = 16;        // rows per wavefront
+  constexpr int NST = 2;        // LDS stages (K + V of one tile each)
+  constexpr int P = kQueryLead;  // tiles in flight per loader thread
+  constexpr int NT = 8;         // address-table slots (>= P + 2)
+  static_assert(NT >= P + 2 && (NT & (NT - 1)) == 0, "table ring");
+  static_assert(CP <= NL, "one (row, chunk pair) per loader thread");
   constexpr uint8_t kRot = 1, kNew = 2;
   constexpr int H = D / 2;
-  // Rotation work items (row, chunk pair) per thread; each thread keeps the
-  // angles of its fixed row offsets in registers when it has at most two.
-  constexpr int IPT = (kKeyTile * CP + 64 * NL - 1) / (64 * NL);
-  constexpr bool KEEP_B = IPT <= 2;
   __shared__ __align__(16) char lds[NST * Gm::STAGE];
-  __shared__ __align__(16) f32x2 rot_a[NST][kMaxHalf];  // cos / sin of w_i * u0 per stage
+  __shared__ __align__(16) f32x2 rot_a[NT][kMaxHalf];  // cos / sin of w_i * u0 per tile
+  __shared__ __align__(16) f32x2 rot_b[kKeyTile][H];    // cos / sin of w_i * row
   __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
-  __shared__ uint64_t row_k[NST][kKeyTile], row_v[NST][kKeyTile];
-  __shared__ int32_t row_dst[NST][kKeyTile];
-  __shared__ uint8_t row_flag[NST][kKeyTile];
-  __shared__ uint8_t tile_flag[2 * NST];  // indexed by tile % 8 (see plan)
+  __shared__ uint64_t row_k[NT][kKeyTile], row_v[NT][kKeyTile];
+  __shared__ int32_t row_dst[NT][kKeyTile];
+  __shared__ uint8_t row_flag[NT][kKeyTile];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool loader = wave >= NWA;
@@ -233,187 +313,137 @@ __global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf1
   const int it0 = split * a.tiles_per_split;
   const int cnt = max(0, min(it0 + a.tiles_per_split, n_tiles) - it0);
 
-  // Per-source base addresses (bf16 elements -> bytes) and row strides.
-  const uint64_t kb0 = reinterpret_cast<uint64_t>(a.k_pool), vb0 = reinterpret_cast<uint64_t>(a.v_pool);
-  const uint64_t kb1 = reinterpret_cast<uint64_t>(a.k_ctx), vb1 = reinterpret_cast<uint64_t>(a.v_ctx);
-  const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
-  const int64_t tok0_1 = (int64_t)b * a.cap, tok0_2 = (int64_t)b * a.n_new;
+  if (loader) {
+    TilePlanner<D, NT> tp(a, b, g, T, nseg, dst0, it0, lane);
+    auto plan = [&](int li) {
+      if (wave == NWA) tp.plan(li, lane, seg_start, seg_src, seg_buf, row_k, row_v, row_flag, row_dst, rot_a);
+    };
 
-  const double fa = a.freq.rev[lane % H];  // loader wavefront 0: tile angle of frequency `lane`
-  // Row sources of local tile li (wavefront 0, one row per lane).  The tile
-  // flags are double-buffered over 8 tiles: a slow wavefront may still read
-  // tile li-1's flag while tile li+3's is being written.
-  // Row sources of local tile li (loader wavefront 0, one row per lane).
-  // The tile flags are double-buffered over 8 tiles: a slow wavefront may
-  // still read tile li-1's flag while tile li+3's is being written.  The
-  // tiles are planned in order, so each lane follows its row's segment
-  // forward from the previous tile instead of searching for it.
-  int s_cur = -1;
-  auto plan = [&](int li) {
-    if (wave == NWA) {
-      const int u_real = (it0 + li) * kKeyTile + lane;
-      const bool real = u_real < T;
-      const int u = min(u_real, T - 1);  // rows past the context repeat the last row (masked)
-      if (s_cur < 0) {
-        s_cur = upper_index(seg_start, nseg, u);
-      } else {
-        while (s_cur + 1 < nseg && seg_start[s_cur + 1] <= u) ++s_cur;
-      }
-      const int s = s_cur;
-      const int64_t tok = seg_src[s] + (u - seg_start[s]);
-      const int buf = seg_buf[s];
-      // Branch-free select of the source (a pointer select here is otherwise
-      // lowered to a lookup table in scratch memory).
-      const uint64_t m0 = buf == 0 ? ~0ull : 0ull, m1 = buf == 1 ? ~0ull : 0ull;
-      const uint64_t m2 = ~(m0 | m1);
-      const int64_t trow = (buf == 0 ? 0 : buf == 1 ? tok0_1 : tok0_2) + tok;
-      const uint64_t off = 2ull * static_cast<uint64_t>((trow * a.hkv + g) * D);
-      const int slot = li % NST;
-      row_k[slot][lane] = ((kb0 & m0) | (kb1 & m1) | (kb2 & m2)) + off;
-      row_v[slot][lane] = ((vb0 & m0) | (vb1 & m1) | (vb2 & m2)) + off;
-      const uint8_t f = real ? (buf != 1 ? kRot : 0) | (buf == 2 ? kNew : 0) : 0;
-      row_flag[slot][lane] = f;
-      row_dst[slot][lane] = dst0 + (int)tok;
-      if (lane < H) {
-        float c, sn;
-        rope_cs((int64_t)(it0 + li) * kKeyTile, fa, c, sn);
-        rot_a[slot][lane] = f32x2{c, sn};
-      }
-      const uint64_t any_rot = __builtin_amdgcn_ballot_w64(f & kRot);
-      const uint64_t any_new = __builtin_amdgcn_ballot_w64(f & kNew);
-      if (lane == 0) tile_flag[li & (2 * NST - 1)] = (any_rot ? kRot : 0) | (any_new ? kNew : 0);
+    // This thread's (row, chunk pair): chunks c and c + CP of one row of
+    // every tile (the two halves RoPE pairs up).  With fewer pairs than
+    // loader threads the rest load a copy and store nothing (loads stay
+    // unconditional, so the compiler's completion counts stay exact).
+    const bool active = kKeyTile * CP == 64 * NL || ltid < kKeyTile * CP;
+    const int item = ltid % (kKeyTile * CP);
+    const int row = item / CP, c = item % CP;
+    const int ko1 = row * Gm::ROW + Gm::k_phys(row, c) * 16;
+    const int ko2 = row * Gm::ROW + Gm::k_phys(row, c + CP) * 16;
+    const int vo1 = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, c) * 16;
+    const int vo2 = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, c + CP) * 16;
+    for (int i = ltid; i < kKeyTile * H; i += 64 * NL) {
+      float cb, sb;
+      rope_cs(i / H, a.freq.rev[i % H], cb, sb);
+      rot_b[i / H][i % H] = f32x2{cb, sb};
     }
-  };
-  // Loads of local tile li into its stage (all waves).
-  auto load = [&](int li) {
-    const int slot = li % NST;
-    char* st = lds + slot * Gm::STAGE;
-    const uint16_t* src[LPW];
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int i = (wave - NWA) + j * NL;  // 0 .. 2*INSTR-1
-      const int mat = i / INSTR, ii = i - mat * INSTR;
-      const int off = ii * 1024 + lane * 16;
-      const int row = off / Gm::ROW, p = (off % Gm::ROW) >> 4;
-      const int c = mat == 0 ? Gm::k_phys(row, p) : Gm::v_phys(row, p);
-      src[j] = reinterpret_cast<const uint16_t*>(mat == 0 ? row_k[slot][row] : row_v[slot][row]) +
-               c * 8;
-    }
-    // All table reads first, then the loads back to back.
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int i = (wave - NWA) + j * NL;
-      const int mat = i / INSTR, ii = i - mat * INSTR;
-      dma16(src[j], st + mat * Gm::KBYTES + ii * 1024);
-    }
-  };
+    const bool writer = rg == 0;  // one row group writes the new tokens back
 
-  Flash16<D> fl;
-  fl.init();
-  int koff[KS], vbase[OT];
-  lane_offsets16<D>(lane, kh * KH, koff, vbase);
-  // The in-LDS rotation handles chunk pair tid % CP of its rows: its 8
-  // frequencies, and the angles of its fixed row offsets, live in registers
-  // (no per-lane kernel-argument loads in the loop, whose vector-memory
-  // counter is reserved for the tile loads).
-  double fr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) fr[i] = a.freq.rev[8 * (ltid % CP) + i];
-  float rb_c[KEEP_B ? IPT : 1][8], rb_s[KEEP_B ? IPT : 1][8];
-  if constexpr (KEEP_B) {
-#pragma unroll
-    for (int k = 0; k < IPT; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rope_cs(((ltid + k * 64 * NL) / CP) & (kKeyTile - 1), fr[i], rb_c[k][i], rb_s[k][i]);
-  }
-  const bool writer = rg == 0;  // one row group writes the new tokens back
-
-  // RoPE at the virtual position for pool rows and new tokens of local tile
-  // li, in LDS; the new tokens' rotated K (from registers) and V go to the
-  // context buffer.  Runs one tile ahead of the attention (see the loop).
-  auto rotate = [&](int li) {
-    const int slot = li % NST;
-    if (!(tile_flag[li & (2 * NST - 1)] & kRot)) return;
-    char* st = lds + slot * Gm::STAGE;
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const int uidx = ltid + k * 64 * NL;
-      if (uidx >= kKeyTile * CP) break;
-      const int row = uidx / CP, c = uidx - row * CP;
+    u32x4 kr[P][2], vr[P][2];
+    auto issue = [&](auto set, int li) {
+      constexpr int S = decltype(set)::value;
+      const int slot = li & (NT - 1);
+      // Global (not flat) loads: flat ones would also count against the LDS
+      // counter that every barrier below waits for.
+      typedef const __attribute__((address_space(1))) u32x4* gptr;
+      const gptr kp = reinterpret_cast<gptr>(row_k[slot][row]);
+      const gptr vp = reinterpret_cast<gptr>(row_v[slot][row]);
+      kr[S][0] = kp[c];
+      kr[S][1] = kp[c + CP];
+      vr[S][0] = vp[c];
+      vr[S][1] = vp[c + CP];
+    };
+    // Rotate tile li's K pair at u0 + row (tile angle + row angle) and store
+    // K and V into the tile's stage; new tokens also go to the context buffer.
+    auto store = [&](auto set, int li) {
+      constexpr int S = decltype(set)::value;
+      if (!active) return;
+      const int slot = li & (NT - 1);
+      char* st = lds + (li % NST) * Gm::STAGE;
+      u32x4 x1 = kr[S][0], x2 = kr[S][1];
       const uint8_t f = row_flag[slot][row];
-      if (!(f & kRot)) continue;
-      u32x4* k1 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c) * 16);
-      u32x4* k2 = reinterpret_cast<u32x4*>(st + row * Gm::ROW + Gm::k_phys(row, c + CP) * 16);
-      u32x4 x1 = *k1, x2 = *k2;
-      // angle(u0 + row) = angle(u0) (tile table) + angle(row) (registers).
-      float cs[8], sn[8];
-      const f32x4* ap = reinterpret_cast<const f32x4*>(&rot_a[slot][8 * c]);
+      if (f & kRot) {
+        // (rotate_pair written out: as a call the compiler keeps more of the
+        // angle reads live at once.)
+        const f32x4* ap = reinterpret_cast<const f32x4*>(&rot_a[slot][8 * c]);
+        const f32x4* bp = reinterpret_cast<const f32x4*>(&rot_b[row][8 * c]);
+        uint32_t wa[4] = {x1.x, x1.y, x1.z, x1.w}, wb[4] = {x2.x, x2.y, x2.z, x2.w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const f32x4 av = ap[h];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = 2 * h + e;
-          float cb, sb;
-          if constexpr (KEEP_B) {
-            cb = rb_c[k][i];
-            sb = rb_s[k][i];
-          } else {
-            rope_cs(row, fr[i], cb, sb);
-          }
-          angle_add(av[2 * e], av[2 * e + 1], cb, sb, cs[i], sn[i]);
+        for (int h = 0; h < 4; ++h) {
+          if (h == 2) __builtin_amdgcn_sched_barrier(0);
+          const f32x4 av = ap[h], bv = bp[h];
+          float c0, s0, c1, s1;
+          angle_add(av[0], av[1], bv[0], bv[1], c0, s0);
+          angle_add(av[2], av[3], bv[2], bv[3], c1, s1);
+          const float a0 = bf16_lo(wa[h]), a1 = bf16_hi(wa[h]);
+          const float b0 = bf16_lo(wb[h]), b1 = bf16_hi(wb[h]);
+          wa[h] = pack_bf16x2(rot_lo(a0, b0, c0, s0), rot_lo(a1, b1, c1, s1));
+          wb[h] = pack_bf16x2(rot_hi(a0, b0, c0, s0), rot_hi(a1, b1, c1, s1));
         }
+        x1 = u32x4{wa[0], wa[1], wa[2], wa[3]};
+        x2 = u32x4{wb[0], wb[1], wb[2], wb[3]};
       }
-      rotate_chunk(x1, x2, cs, sn);
-      *k1 = x1;
-      *k2 = x2;
+      *reinterpret_cast<u32x4*>(st + ko1) = x1;
+      *reinterpret_cast<u32x4*>(st + ko2) = x2;
+      *reinterpret_cast<u32x4*>(st + vo1) = vr[S][0];
+      *reinterpret_cast<u32x4*>(st + vo2) = vr[S][1];
       if ((f & kNew) && writer) {
+        keep_branch();
         const int64_t d = (((int64_t)b * a.cap + row_dst[slot][row]) * a.hkv + g) * CR;
         u32x4* ko = static_cast<u32x4*>(a.k_ctx);
         u32x4* vo = static_cast<u32x4*>(a.v_ctx);
-        const char* vs = st + Gm::KBYTES + row * Gm::ROW;
         ko[d + c] = x1;
         ko[d + c + CP] = x2;
-        vo[d + c] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c) * 16);
-        vo[d + c + CP] = *reinterpret_cast<const u32x4*>(vs + Gm::v_phys(row, c + CP) * 16);
+        vo[d + c] = vr[S][0];
+        vo[d + c + CP] = vr[S][1];
       }
-    }
-  };
+    };
 
-  // Loader and attention wavefronts run separate loops (so their loop state
-  // can share registers) that meet at the same barriers: one per tile, after
-  // which the loaders request tile li+3 into the stage tile li-1 left and
-  // rotate tile li+1 while the attention wavefronts use tile li.
-  if (loader) {
-    for (int li = 0; li < NST - 1 && li < cnt; ++li) plan(li);
+    // Barriers shared with the attention wavefronts: one after the plans of
+    // tiles 0..P, one after tile 0 is stored, then one per later tile.
+    for (int li = 0; li <= P; ++li) plan(li);
     waitcnt<0, 0>();
     barrier_nofence();
-    for (int li = 0; li < NST - 1 && li < cnt; ++li) load(li);
     if (cnt > 0) {
-      wait_vm<true>(LPW * min(NST - 2, cnt - 1));  // tile 0 landed
+      static_for<P>([&](auto t) { issue(t, (int)decltype(t)::value); });
+      store(std::integral_constant<int, 0>{}, 0);
+      waitcnt<63, 0>();
       barrier_nofence();
-      rotate(0);
     }
-    for (int li = 0; li < cnt; ++li) {
-      if (li + NST - 1 < cnt) plan(li + NST - 1);
-      // Tile li+1 landed (only tile li+2's loads may fly; the rotation's LDS
-      // writes are done too); the barrier publishes tile li's rotation and
-      // the new address table, and frees tile li-1's stage for the refill.
-      wait_vm<true>(LPW * max(0, min(NST - 3, cnt - 2 - li)));
-      barrier_nofence();
-      if (li + NST - 1 < cnt) load(li + NST - 1);
-      if (li + 1 < cnt) rotate(li + 1);
+    // Iteration li (the attention uses tile li): request tile li + P into
+    // the register set tile li left, plan tile li + P + 1, store tile li + 1
+    // into the stage tile li - 1 left.  Whole groups of P iterations run
+    // without branches around the loads; the last < P iterations follow.
+    int l0 = 0;
+    for (; l0 + P < cnt; l0 += P) {
+      static_for<P>([&](auto t) {
+        constexpr int S = decltype(t)::value;
+        issue(t, l0 + S + P);
+        plan(l0 + S + P + 1);
+        store(std::integral_constant<int, (S + 1) % P>{}, l0 + S + 1);
+        waitcnt<63, 0>();
+        barrier_nofence();
+      });
     }
+    static_for<P>([&](auto t) {
+      constexpr int S = decltype(t)::value;
+      if (l0 + S + 1 < cnt) {
+        store(std::integral_constant<int, (S + 1) % P>{}, l0 + S + 1);
+        waitcnt<63, 0>();
+        barrier_nofence();
+      }
+    });
     if constexpr (KSPL == 2) {  // the attention wavefronts' merge below
       __syncthreads();
       __syncthreads();
     }
     return;
   }
+
+  Flash16<D> fl;
+  fl.init();
+  int koff[KS], vbase[OT];
+  lane_offsets16<D>(lane, kh * KH, koff, vbase);
   waitcnt<0, 0>();
   barrier_nofence();
-  if (cnt > 0) barrier_nofence();
   for (int li = 0; li < cnt; ++li) {
     waitcnt<0, 0>();  // this wavefront's reads of tile li-1 are done
     barrier_nofence();
@@ -474,6 +504,333 @@ __global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf1
 #pragma unroll
     for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t + 4 * q16) = fl.o[t];
     if (q16 == 0) {
+      a.part_ml[prow * 2 + 0] = fl.m;
+      a.part_ml[prow * 2 + 1] = lsum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query attention for many packed rows (GQA groups times query tokens), bf16
+// MFMA, split-K over the context.
+//
+// Workgroup = NWA attention wavefronts of 32 packed rows each (the software-
+// pipelined Flash core of the prefill, on v_mfma_f32_32x32x16_bf16) plus
+// kWideLoaders loader wavefronts, one of each kind per SIMD: a 32-row
+// attention wavefront needs half of a SIMD's registers.  Iteration i of the
+// attention computes the softmax of tile i, P V of tile i - 1 and the scores
+// of tile i + 1, so it reads K of tile i + 1 and V of tile i - 1; meanwhile
+// the loaders store K and V of tile i + 2 (K ring of two LDS stages, V ring
+// of four).  Each loader thread owns two (row, chunk pair) items of every
+// tile: it follows its rows through the segment list in registers, keeps
+// every tile's K and V in registers kLead tiles ahead of its store (the
+// compiler counts these loads, so every store waits for exactly its own
+// tile) and rotates K at the row's virtual position on the way to LDS (row
+// angles in registers, the tile's angles from a small table).  New tokens
+// (their rotated K and their V) also go to the context buffer.
+// ---------------------------------------------------------------------------
+template <int D, int NWA>
+__global__ __launch_bounds__(64 * (NWA + kWideLoaders), 1) void k_query_wide_bf16(QueryArgs a) {
+  using Gm = TileGeom<D>;
+  constexpr int NL = kWideLoaders, NW = NWA + NL;
+  constexpr int KS = D / 16, OT = D / 32, CP = D / 16, CR = D / 8, H = D / 2;
+  constexpr int P = kWideLead;
+  constexpr int NT = 8;  // tile-angle table slots
+  static_assert(NT >= P + 2 && (NT & (NT - 1)) == 0, "angle table ring");
+  constexpr int ITEMS = kKeyTile * CP / (64 * NL);  // (row, chunk pair) items per loader thread
+  static_assert(ITEMS >= 1 && ITEMS * 64 * NL == kKeyTile * CP, "items split evenly");
+  constexpr int NVS = 4;  // V stages
+  __shared__ __align__(16) char kring[2 * Gm::KBYTES];
+  __shared__ __align__(16) char vring[NVS * Gm::VBYTES];
+  __shared__ __align__(16) f32x2 rot_a[NT][kMaxHalf];  // cos / sin of w_i * u0 per tile
+  __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool loader = wave >= NWA;
+  const int hh = lane >> 5, col = lane & 31;
+  // Work item (split, KV head g, row group rg, batch row b).  With several
+  // row groups, those of one (split, head, batch row) take consecutive
+  // workgroup slots of one XCD (ids 8 apart: the hardware deals consecutive
+  // ids to the 8 XCDs in turn), so they run side by side and the second
+  // load of every tile hits that XCD's L2 instead of HBM.
+  const int R = a.row_groups, W = a.n_split * a.hkv * a.batch;
+  const int lin = blockIdx.x;
+  const int rg = R > 1 ? (lin >> 3) % R : 0;
+  const int w = R > 1 ? (lin / (8 * R)) * 8 + (lin & 7) : lin;
+  if (w >= W) return;  // padding of the last group of 8 (before any barrier)
+  const int g = w % a.hkv, split = (w / a.hkv) % a.n_split, b = w / (a.hkv * a.n_split);
+  const int G = a.hq / a.hkv;
+  const int rho = rg * (32 * NWA) + wave * 32 + col;
+  const bool live = !loader && rho < a.rows;
+  const int r = live ? rho / G : 0;
+  const int head = g * G + (live ? rho - (rho / G) * G : 0);
+  const int32_t* tab = seg_block(a);
+  const int pos0 = tab[a.seg.o_pos0 + b];
+  const int dst0 = tab[a.seg.o_dst + b];
+  const int qpos = pos0 + r;
+
+  const int nseg = tab[a.seg.o_nseg + b];
+  {
+    const int32_t* st = tab + a.seg.o_start + b * a.seg.stride;
+    const int32_t* sr = tab + a.seg.o_src + b * a.seg.stride;
+    const int32_t* sb = tab + a.seg.o_buf + b * a.seg.stride;
+    for (int i = tid; i <= nseg; i += 64 * NW) {
+      seg_start[i] = st[i];
+      if (i < nseg) {
+        seg_src[i] = sr[i];
+        seg_buf[i] = sb[i];
+      }
+    }
+  }
+  __syncthreads();  // segment table visible
+
+  const int T = seg_start[nseg];
+  const int n_tiles = (T + kKeyTile - 1) / kKeyTile;
+  const int it0 = split * a.tiles_per_split;
+  const int cnt = max(0, min(it0 + a.tiles_per_split, n_tiles) - it0);
+
+  if (loader) {
+    const int ltid = tid - 64 * NWA;
+    if (cnt == 0) {
+      barrier_nofence();
+      return;
+    }
+    // Item k of this thread: row ltid / CP + k * 64 / ITEMS, chunks c and
+    // c + CP (the two halves RoPE pairs up).
+    const int c = ltid % CP;
+    const uint64_t kb0 = reinterpret_cast<uint64_t>(a.k_pool), vb0 = reinterpret_cast<uint64_t>(a.v_pool);
+    const uint64_t kb1 = reinterpret_cast<uint64_t>(a.k_ctx), vb1 = reinterpret_cast<uint64_t>(a.v_ctx);
+    const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
+    const int64_t tok0_1 = (int64_t)b * a.cap, tok0_2 = (int64_t)b * a.n_new;
+    const double fa = a.freq.rev[lane % H];  // first loader wavefront: tile angle of frequency `lane`
+    int rows[ITEMS], ko1[ITEMS], ko2[ITEMS], vo1[ITEMS], vo2[ITEMS];
+    // Segment followed by each item's row: index and end, and the row
+    // address (K, and V - K) and flags of position 0 in that segment's
+    // coordinates, so that a tile only adds u * row stride.
+    const int64_t rstride = (int64_t)a.hkv * D * 2;  // bytes per token row
+    int sidx[ITEMS], send[ITEMS], fbase[ITEMS];
+    uint64_t kaddr0[ITEMS], vdelta[ITEMS];
+    auto enter = [&](auto kk, int sg) __attribute__((always_inline)) {
+      constexpr int k = decltype(kk)::value;
+      sidx[k] = sg;
+      send[k] = seg_start[sg + 1];
+      const int buf = seg_buf[sg];
+      const int64_t sbase = (int64_t)seg_src[sg] - seg_start[sg];  // token = sbase + u
+      // Branch-free select of the source (a pointer select here is
+      // otherwise lowered to a lookup table in scratch memory).
+      const uint64_t m0 = buf == 0 ? ~0ull : 0ull, m1 = buf == 1 ? ~0ull : 0ull;
+      const uint64_t m2 = ~(m0 | m1);
+      const uint64_t kb = (kb0 & m0) | (kb1 & m1) | (kb2 & m2);
+      const uint64_t vb = (vb0 & m0) | (vb1 & m1) | (vb2 & m2);
+      const int64_t trow0 = (buf == 0 ? 0 : buf == 1 ? tok0_1 : tok0_2) + sbase;
+      kaddr0[k] = kb + static_cast<uint64_t>(trow0 * rstride + (int64_t)g * D * 2);
+      vdelta[k] = vb - kb;
+      // 4 * (context-buffer row - u) + (new << 1) + rotate
+      fbase[k] = (int)((((uint32_t)dst0 + (uint32_t)sbase) << 2) | (buf == 2 ? 2u : 0u) |
+                       (buf != 1 ? 1u : 0u));
+    };
+    float rb_c[ITEMS][8], rb_s[ITEMS][8];  // angles of the row offset
+    static_for<ITEMS>([&](auto kk) __attribute__((always_inline)) {
+      constexpr int k = decltype(kk)::value;
+      const int row = ltid / CP + k * (kKeyTile / ITEMS);
+      rows[k] = row;
+      ko1[k] = row * Gm::ROW + Gm::k_phys(row, c) * 16;
+      ko2[k] = row * Gm::ROW + Gm::k_phys(row, c + CP) * 16;
+      vo1[k] = row * Gm::ROW + Gm::v_phys(row, c) * 16;
+      vo2[k] = row * Gm::ROW + Gm::v_phys(row, c + CP) * 16;
+      enter(kk, upper_index(seg_start, nseg, min(it0 * kKeyTile + row, T - 1)));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rope_cs(row, a.freq.rev[8 * c + i], rb_c[k][i], rb_s[k][i]);
+    });
+    const bool writer = rg == 0;  // one row group writes the new tokens back
+    typedef const __attribute__((address_space(1))) u32x4* gptr;  // global, not flat, loads
+    u32x4 kr[P][ITEMS][2], vr[P][ITEMS][2];
+    int fl[P][ITEMS];  // per tile and item: 4 * context-buffer row + (new << 1) + rotate
+    // Loads of tile t into register set S (tiles past the split repeat the
+    // context's last row, so the loads never need a branch); the first
+    // loader wavefront also writes the tile's angles.
+    auto issue = [&](auto set, int t) __attribute__((always_inline)) {
+      constexpr int S = decltype(set)::value;
+      static_for<ITEMS>([&](auto kk) __attribute__((always_inline)) {
+        constexpr int k = decltype(kk)::value;
+        const int u_real = (it0 + t) * kKeyTile + rows[k];
+        const int u = min(u_real, T - 1);
+        while (u >= send[k]) enter(kk, sidx[k] + 1);
+        const uint64_t ka = kaddr0[k] + static_cast<uint64_t>((int64_t)u * rstride);
+        const gptr kp = reinterpret_cast<gptr>(ka);
+        const gptr vp = reinterpret_cast<gptr>(ka + vdelta[k]);
+        kr[S][k][0] = kp[c];
+        kr[S][k][1] = kp[c + CP];
+        vr[S][k][0] = vp[c];
+        vr[S][k][1] = vp[c + CP];
+        fl[S][k] = u_real < T ? (int)((uint32_t)fbase[k] + ((uint32_t)u << 2)) : 0;
+      });
+      if (wave == NWA && lane < H) {
+        float cs, sn;
+        rope_cs((int64_t)(it0 + t) * kKeyTile, fa, cs, sn);
+        rot_a[t & (NT - 1)][lane] = f32x2{cs, sn};
+      }
+    };
+    // Tile t from register set S: rotate K at u0 + row, store K and V into
+    // the tile's stages; new tokens also go to the context buffer.
+    auto store = [&](auto set, int t) __attribute__((always_inline)) {
+      constexpr int S = decltype(set)::value;
+      char* sk = kring + (t & 1) * Gm::KBYTES;
+      char* sv = vring + (t & (NVS - 1)) * Gm::VBYTES;
+      const f32x4* ap = reinterpret_cast<const f32x4*>(&rot_a[t & (NT - 1)][8 * c]);
+      f32x4 av[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) av[h] = ap[h];  // the same 8 frequencies for every item
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) {
+        u32x4 x1 = kr[S][k][0], x2 = kr[S][k][1];
+        const int f = fl[S][k];
+        if (f & 1) {
+          uint32_t wa[4] = {x1.x, x1.y, x1.z, x1.w}, wb[4] = {x2.x, x2.y, x2.z, x2.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            float c0, s0, c1, s1;
+            angle_add(av[h][0], av[h][1], rb_c[k][2 * h], rb_s[k][2 * h], c0, s0);
+            angle_add(av[h][2], av[h][3], rb_c[k][2 * h + 1], rb_s[k][2 * h + 1], c1, s1);
+            const float a0 = bf16_lo(wa[h]), a1 = bf16_hi(wa[h]);
+            const float b0 = bf16_lo(wb[h]), b1 = bf16_hi(wb[h]);
+            wa[h] = pack_bf16x2(rot_lo(a0, b0, c0, s0), rot_lo(a1, b1, c1, s1));
+            wb[h] = pack_bf16x2(rot_hi(a0, b0, c0, s0), rot_hi(a1, b1, c1, s1));
+          }
+          x1 = u32x4{wa[0], wa[1], wa[2], wa[3]};
+          x2 = u32x4{wb[0], wb[1], wb[2], wb[3]};
+        }
+        *reinterpret_cast<u32x4*>(sk + ko1[k]) = x1;
+        *reinterpret_cast<u32x4*>(sk + ko2[k]) = x2;
+        *reinterpret_cast<u32x4*>(sv + vo1[k]) = vr[S][k][0];
+        *reinterpret_cast<u32x4*>(sv + vo2[k]) = vr[S][k][1];
+        if ((f & 2) && writer) {
+          keep_branch();
+          const int64_t d = (((int64_t)b * a.cap + ((uint32_t)f >> 2)) * a.hkv + g) * CR;
+          u32x4* ko = static_cast<u32x4*>(a.k_ctx);
+          u32x4* vo = static_cast<u32x4*>(a.v_ctx);
+          ko[d + c] = x1;
+          ko[d + c + CP] = x2;
+          vo[d + c] = vr[S][k][0];
+          vo[d + c + CP] = vr[S][k][1];
+        }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // Barriers shared with the attention wavefronts: after tiles 0 and 1
+    // are stored, after the scores of tile 0, then one per iteration.
+    static_for<P>([&](auto t) __attribute__((always_inline)) { issue(t, (int)decltype(t)::value); });
+    waitcnt<63, 0>();
+    barrier_nofence();  // tile angles of tiles 0 .. P - 1 visible
+    store(I0{}, 0);
+    store(I1{}, 1);
+    issue(I0{}, P);
+    waitcnt<63, 0>();
+    barrier_nofence();
+    barrier_nofence();
+    // Iteration i (K of tile i + 1 and V of tile i - 1 in use): request tile
+    // i + 1 + P into the register set tile i + 1 left, store tile i + 2.
+    // Whole groups of P iterations run without branches around the loads
+    // (tiles stored past the split go to stages no product uses).
+    auto step = [&](auto t, int i) __attribute__((always_inline)) {
+      constexpr int S = decltype(t)::value;
+      issue(std::integral_constant<int, (S + 1) % P>{}, i + 1 + P);
+      store(std::integral_constant<int, (S + 2) % P>{}, i + 2);
+      waitcnt<63, 0>();
+      barrier_nofence();
+    };
+    int l0 = 0;
+    for (; l0 + P <= cnt; l0 += P)
+      static_for<P>([&](auto t) __attribute__((always_inline)) { step(t, l0 + (int)decltype(t)::value); });
+    static_for<P>([&](auto t) __attribute__((always_inline)) {
+      if (l0 + (int)decltype(t)::value < cnt) step(t, l0 + (int)decltype(t)::value);
+    });
+    return;
+  }
+
+  // Attention wavefront: rows rho of the group; Q rotated at its position.
+  bf16x8 qb[KS];
+  {
+    u32x4 raw[KS];
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.n_new + r) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], qpos, a.freq, 16 * ks + 8 * hh, a.q_scale);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+  Flash<D> fl;
+  fl.init();
+  int koff[KS], vbase[OT];
+  lane_offsets<D>(lane, koff, vbase);
+  const auto kst = [&](int i) { return kring + (i & 1) * Gm::KBYTES; };
+  const auto vst = [&](int i) { return vring + (i & (NVS - 1)) * Gm::VBYTES; };
+  // Only tiles reaching past the first query token can hide keys from a row
+  // (causal among the new tokens; rows past the context are all masked).
+  const auto mask_of = [&](int i) { return (it0 + i) * kKeyTile + kKeyTile - 1 > pos0; };
+  const auto vis_of = [&](int i) {
+    const int lim = qpos - (it0 + i) * kKeyTile;
+    return [=](int kr) { return kr <= lim; };
+  };
+  if (cnt == 0) {
+    barrier_nofence();
+  } else {
+    barrier_nofence();  // (the loaders' tile angles)
+    barrier_nofence();  // tiles 0 and 1 stored
+    f32x16 s0, s1, n0, n1;
+    bf16x8 pr[4];
+    fl.scores(kst(0), koff, qb, s0, s1);
+    waitcnt<0, 0>();
+    barrier_nofence();
+    fl.template pv_head<false>(vst(0), vbase, pr, s0, s1, mask_of(0), vis_of(0));
+    fl.exp_next(kst(1), koff, qb, s0, s1, pr, n0, n1);
+    // Two iterations per trip so the score registers alternate.
+    for (int i = 1; i < cnt; i += 2) {
+      waitcnt<0, 0>();
+      barrier_nofence();
+      fl.template pv_head<true>(vst(i - 1), vbase, pr, n0, n1, mask_of(i), vis_of(i));
+      fl.exp_next(kst(i + 1), koff, qb, n0, n1, pr, s0, s1);
+      if (i + 1 >= cnt) break;
+      waitcnt<0, 0>();
+      barrier_nofence();
+      fl.template pv_head<true>(vst(i), vbase, pr, s0, s1, mask_of(i + 1), vis_of(i + 1));
+      fl.exp_next(kst(i + 2), koff, qb, s0, s1, pr, n0, n1);
+    }
+    waitcnt<0, 0>();
+    barrier_nofence();
+    fl.pv(vst(cnt - 1), vbase, pr);
+  }
+  const float lsum = fl.total();
+  if (!live) return;
+  if (a.n_split == 1) {
+    const float inv = 1.0f / lsum;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
+#pragma unroll
+    for (int m = 0; m < OT; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = m * 32 + q4 * 8 + hh * 4;
+        const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
+                         pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d) = w;
+      }
+  } else {
+    const int64_t prow = (((int64_t)b * a.hkv + g) * a.n_split + split) * a.rows + rho;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int m = 0; m < OT; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = m * 32 + q4 * 8 + hh * 4;
+        *reinterpret_cast<f32x4*>(po + d) = f32x4{fl.o[m][4 * q4 + 0], fl.o[m][4 * q4 + 1],
+                                                  fl.o[m][4 * q4 + 2], fl.o[m][4 * q4 + 3]};
+      }
+    if (hh == 0) {
       a.part_ml[prow * 2 + 0] = fl.m;
       a.part_ml[prow * 2 + 1] = lsum;
     }
@@ -655,11 +1012,19 @@ hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
 
 template <int D>
 static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.wide) {
+    const int w = a.n_split * a.hkv * grid.z;
+    grid = dim3(a.row_groups > 1 ? (w + 7) / 8 * 8 * a.row_groups : w);
+    switch (a.row_waves) {
+      case 3: hipLaunchKernelGGL((k_query_wide_bf16<D, 3>), grid, dim3(64 * (3 + kWideLoaders)), 0, stream, a); break;
+      default: hipLaunchKernelGGL((k_query_wide_bf16<D, 4>), grid, dim3(64 * (4 + kWideLoaders)), 0, stream, a); break;
+    }
+    return;
+  }
   switch (a.row_waves) {
     case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(64 * (2 + kQueryLoaders)), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(64 * (4 + kQueryLoaders)), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_query_bf16<D, 8, 1>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
   }
 }
 
@@ -671,8 +1036,9 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     else hipLaunchKernelGGL(k_query_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  if (a.row_waves != 1 && a.row_waves != 2 && a.row_waves != 4 && a.row_waves != 8)
-    return hipErrorInvalidValue;
+  const bool ok = a.wide ? a.row_waves == 3 || a.row_waves == 4
+                        : a.row_waves == 1 || a.row_waves == 2 || a.row_waves == 4;
+  if (!ok) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
   if (head_dim == 128) launch_query_d<128>(a, grid, stream);
   else launch_query_d<64>(a, grid, stream);

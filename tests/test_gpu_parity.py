@@ -242,6 +242,21 @@ def test_query_attn_gqa_many_rows_and_split():
         _stage2_case("bf16", 16, 4, 128, lens, ids, 64, 5e5, 111, fused)
 
 
+def test_query_wide_rows_head_dim_64_and_three_waves():
+    """Many packed rows per KV head on the 32-row kernels: head_dim 64 with
+    two row groups of 80 rows (3 wavefronts each), and head_dim 128 with 76
+    rows in one group; both fused and materialised, split and unsplit."""
+    rng = np.random.default_rng(43)
+    lens = rng.integers(30, 300, size=10).astype(np.int32)
+    ids = np.array([[0, 2, 3, 7, 9], [0, 1, 5, 6, 8]], np.int32)
+    for fused in (False, True):
+        _stage2_case("bf16", 16, 2, 64, lens, ids, 20, 1e4, 191, fused)
+        _stage2_case("bf16", 8, 2, 128, lens, ids[:1], 19, 5e5, 193, fused)
+    long_lens = rng.integers(900, 1500, size=12).astype(np.int32)
+    _stage2_case("bf16", 32, 8, 128, long_lens, np.array([[0, 3, 5, 8, 11]], np.int32), 48, 5e5,
+                 195, True)
+
+
 def test_query_fused_equals_materialised_bitwise():
     rng = np.random.default_rng(23)
     lens = rng.integers(50, 700, size=12).astype(np.int32)
