@@ -290,14 +290,14 @@ void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max
                  QueryPlan& qp) {
   const int G = a->n_q_heads / a->n_kv_heads;
   qp.rows = n_new * G;
-  // Up to 64 rows: 16 packed rows per row wavefront, each key tile split
+  // Up to 32 rows: 16 packed rows per row wavefront, each key tile split
   // between two wavefronts.  More rows: 32-row wavefronts, at most 4 per
-  // workgroup, the rows spread evenly over the fewest row groups (so 65 ..
-  // 128 rows per group: 3 or 4 wavefronts).
-  qp.wide = qp.rows > 64 ? 1 : 0;
+  // workgroup, the rows spread evenly over the fewest row groups (2 .. 4
+  // wavefronts per group).
+  qp.wide = qp.rows > 32 ? 1 : 0;
   if (qp.wide) {
     qp.row_groups = (int32_t)cdiv(qp.rows, 128);
-    qp.row_waves = (int32_t)cdiv(cdiv(qp.rows, qp.row_groups), 32);
+    qp.row_waves = (int32_t)std::max<int64_t>(2, cdiv(cdiv(qp.rows, qp.row_groups), 32));
   } else {
     qp.row_waves = qp.rows <= 16 ? 1 : qp.rows <= 32 ? 2 : 4;
     qp.row_groups = 1;

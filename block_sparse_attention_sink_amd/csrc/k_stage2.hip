@@ -1016,6 +1016,7 @@ static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
     const int w = a.n_split * a.hkv * grid.z;
     grid = dim3(a.row_groups > 1 ? (w + 7) / 8 * 8 * a.row_groups : w);
     switch (a.row_waves) {
+      case 2: hipLaunchKernelGGL((k_query_wide_bf16<D, 2>), grid, dim3(64 * (2 + kWideLoaders)), 0, stream, a); break;
       case 3: hipLaunchKernelGGL((k_query_wide_bf16<D, 3>), grid, dim3(64 * (3 + kWideLoaders)), 0, stream, a); break;
       default: hipLaunchKernelGGL((k_query_wide_bf16<D, 4>), grid, dim3(64 * (4 + kWideLoaders)), 0, stream, a); break;
     }
@@ -1036,7 +1037,7 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     else hipLaunchKernelGGL(k_query_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const bool ok = a.wide ? a.row_waves == 3 || a.row_waves == 4
+  const bool ok = a.wide ? a.row_waves >= 2 && a.row_waves <= 4
                         : a.row_waves == 1 || a.row_waves == 2 || a.row_waves == 4;
   if (!ok) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
