@@ -150,17 +150,12 @@ struct TileGeom {
   }
 };
 
-// This lane's value and its partner's 32 (or 16) lanes away, ordered (lower
-// lane's, upper lane's) in both lanes, by one v_permlane32_swap (or
-// v_permlane16_swap): a vector instruction, where a shuffle would be an LDS
-// permute queued behind the tile reads of the other wavefront on the SIMD.
+// This lane's value and its partner's 32 lanes away, ordered (lower lane's,
+// upper lane's) in both lanes, by one v_permlane32_swap: a vector
+// instruction, where a shuffle would be an LDS permute queued behind the tile
+// reads of the other wavefront on the SIMD.
 __device__ __forceinline__ f32x2 pair_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ f32x2 pair_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
@@ -168,25 +163,9 @@ __device__ __forceinline__ float max_xor32(float x) {
   const f32x2 h = pair_xor32(x);
   return __builtin_fmaxf(h[0], h[1]);
 }
-__device__ __forceinline__ float max_xor16(float x) {
-  const f32x2 h = pair_xor16(x);
-  return __builtin_fmaxf(h[0], h[1]);
-}
 __device__ __forceinline__ float sum_xor32(float x) {
   const f32x2 h = pair_xor32(x);
   return h[0] + h[1];
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const f32x2 h = pair_xor16(x);
-  return h[0] + h[1];
-}
-
-// Eight probabilities of one MFMA result (registers B .. B+7) as a bf16 B operand.
-template <int B>
-__device__ __forceinline__ bf16x8 pack_p(const f32x16 s) {
-  const u32x4 w = u32x4{pack_bf16x2(s[B + 0], s[B + 1]), pack_bf16x2(s[B + 2], s[B + 3]),
-                        pack_bf16x2(s[B + 4], s[B + 5]), pack_bf16x2(s[B + 6], s[B + 7])};
-  return __builtin_bit_cast(bf16x8, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,7 +236,7 @@ struct Flash {
   // A operand of P V product j (k-step kk = j / OT, O^T rows 32t, t = j % OT):
   // two transposed reads of the natural V tile, keys 16kk + 4h + 0..3 and
   // 16kk + 8 + 4h + 0..3 at head dim 32t + col -- the key order in which the
-  // S^T result layout hands out P (see pack_p).
+  // S^T result layout hands out P (see exp_next).
   __device__ __forceinline__ bf16x8 vfrag(const char* st_v, const int (&vbase)[OT], int j) const {
     const char* a0 = st_v + vbase[j % OT] + (16 * (j / OT)) * Gm::ROW;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
@@ -538,145 +517,6 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 16: case 17: case 18: case 19: case 20: case 21: case 22: case 23: waitcnt<16, L>(); break;
     case 24: case 25: case 26: case 27: case 28: case 29: case 30: case 31: waitcnt<24, L>(); break;
     default: if (n >= 32) waitcnt<32, L>(); else waitcnt<0, L>(); break;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Flash-attention state for 16 query rows per wavefront on
-// v_mfma_f32_16x16x32_bf16 (used where rows are few: Stage 2).
-//
-// Lane l owns query row l % 16; its group q = l / 16 holds keys 16j + 4q + i
-// (i = 0..3) of every 16-key subtile j of a 64-key tile (the S^T = K Q^T
-// result layout).  O^T += V^T P^T keeps the output in the same layout:
-// o[t][i] is head dim 16t + 4q + i.  Scores carry scale * log2(e), arrive
-// relative to the reference m and use the same lazy raise as Flash.
-// ---------------------------------------------------------------------------
-template <int D>
-struct Flash16 {
-  static constexpr int KS = D / 32;  // k-steps over the head dim
-  static constexpr int OT = D / 16;  // O^T row tiles
-  using Gm = TileGeom<D>;
-  f32x4 o[OT];
-  float m, l;
-  bool have;
-
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int t = 0; t < OT; ++t) o[t] = f32x4{};
-    m = 0.0f;
-    l = 0.0f;
-    have = false;
-  }
-
-  // KH keys (64 or 32) of one 64-key tile, starting at the key offset folded
-  // into koff / vbase.  koff[ks]: K row l%16, chunk 4ks + q.  vbase[t]: the
-  // transposed V read address for O^T rows 16t.. (row 4q + (l%16)/4).
-  // vis(kr) takes the key index relative to that offset.
-  template <int KH, typename Vis>
-  __device__ __forceinline__ void tile(const char* st, const int (&koff)[KS],
-                                       const int (&vbase)[OT], const bf16x8 (&qb)[KS], bool mask,
-                                       Vis vis) {
-    static_assert(KH == 64 || KH == 32, "32 or 64 keys per wavefront");
-    constexpr int NJ = KH / 16, NK = KH / 32;
-    f32x4 s[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) s[j] = f32x4{-m, -m, -m, -m};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + koff[ks] + 16 * j * Gm::ROW);
-        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], s[j], 0, 0, 0);
-      }
-    const int q = (threadIdx.x >> 4) & 3;
-    if (mask) {
-      keep_branch();
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[j][i] = vis(16 * j + 4 * q + i) ? s[j][i] : kNegInf;
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(s[j][0], s[j][1]),
-                                               __builtin_fmaxf(s[j][2], s[j][3])));
-    mx = max_xor32(max_xor16(mx));
-    const bool need = mx > kLazy || (!have && mx > kNegInf);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      keep_branch();
-      const float delta = need ? mx : 0.0f;
-      const float alpha = have ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
-      m += delta;
-      have = have || mx > kNegInf;
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[j][i] -= delta;
-#pragma unroll
-      for (int t = 0; t < OT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[t][i] *= alpha;
-    }
-    float rs = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[j][i] = __builtin_amdgcn_exp2f(s[j][i]);
-        rs += s[j][i];
-      }
-    l += rs;
-    // k-step kk (32 keys): positions 8q + r <-> keys 32kk + 16 (r/4) + 4q + r%4.
-    bf16x8 p[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 w = u32x4{pack_bf16x2(s[2 * kk][0], s[2 * kk][1]),
-                            pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
-                            pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
-                            pack_bf16x2(s[2 * kk + 1][2], s[2 * kk + 1][3])};
-      p[kk] = __builtin_bit_cast(bf16x8, w);
-    }
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-      for (int t = 0; t < OT; ++t) {
-        const char* a0 = st + vbase[t] + (32 * kk) * Gm::ROW;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a0 + 16 * Gm::ROW));
-        const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
-                                                              hi[0], hi[1], hi[2], hi[3]};
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), p[kk],
-                                                       o[t], 0, 0, 0);
-      }
-  }
-
-  // Row sum over the four lane groups (call once, all lanes).
-  __device__ __forceinline__ float total() const {
-    return sum_xor32(sum_xor16(l));
-  }
-};
-
-// key0 (a multiple of 16) selects the first key of the wavefront's share of
-// the tile; both swizzles depend only on the row modulo 16, so it is a pure
-// row offset.
-template <int D>
-__device__ __forceinline__ void lane_offsets16(int lane, int key0, int (&koff)[D / 32],
-                                               int (&vbase)[D / 16]) {
-  using Gm = TileGeom<D>;
-  const int r16 = lane & 15, q = (lane >> 4) & 3;
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    koff[ks] = (key0 + r16) * Gm::ROW + Gm::k_phys(r16, 4 * ks + q) * 16;
-  const int row = key0 + 4 * q + (r16 >> 2);
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    const int elem = 16 * t + 4 * (lane & 3);
-    vbase[t] = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, elem >> 3) * 16 + (elem & 7) * 2;
   }
 }
 

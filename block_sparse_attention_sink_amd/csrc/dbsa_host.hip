@@ -282,7 +282,7 @@ struct SegPlan {
 };
 
 struct QueryPlan {
-  int32_t rows = 0, wide = 0, row_waves = 4, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  int32_t rows = 0, row_waves = 4, row_groups = 0, n_split = 1, tiles_per_split = 1;
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
@@ -290,18 +290,10 @@ void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max
                  QueryPlan& qp) {
   const int G = a->n_q_heads / a->n_kv_heads;
   qp.rows = n_new * G;
-  // Up to 32 rows: 16 packed rows per row wavefront, each key tile split
-  // between two wavefronts.  More rows: 32-row wavefronts, at most 4 per
-  // workgroup, the rows spread evenly over the fewest row groups (2 .. 4
-  // wavefronts per group).
-  qp.wide = qp.rows > 32 ? 1 : 0;
-  if (qp.wide) {
-    qp.row_groups = (int32_t)cdiv(qp.rows, 128);
-    qp.row_waves = (int32_t)std::max<int64_t>(2, cdiv(cdiv(qp.rows, qp.row_groups), 32));
-  } else {
-    qp.row_waves = qp.rows <= 16 ? 1 : qp.rows <= 32 ? 2 : 4;
-    qp.row_groups = 1;
-  }
+  // 32 packed rows per attention wavefront, at most 4 per workgroup, the rows
+  // spread evenly over the fewest row groups.
+  qp.row_groups = (int32_t)cdiv(qp.rows, 128);
+  qp.row_waves = (int32_t)cdiv(cdiv(qp.rows, qp.row_groups), 32);
   const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
   qp.n_split = 1;
   qp.tiles_per_split = (int32_t)n_tiles;
@@ -404,7 +396,6 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.hkv = a->n_kv_heads;
   qa.batch = batch;
   qa.rows = qp.rows;
-  qa.wide = qp.wide;
   qa.row_waves = qp.row_waves;
   qa.row_groups = qp.row_groups;
   qa.n_split = qp.n_split;

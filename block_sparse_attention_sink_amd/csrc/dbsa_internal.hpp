@@ -18,10 +18,8 @@ constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
 constexpr int kPrefillStages = 4;  // LDS stages per K ring and per V ring
 constexpr int kMaxSegments = 1024;  // context segments per batch row in Stage 2
-constexpr int kQueryLoaders = 8;   // Stage-2 wavefronts that plan, load and rotate tiles
-constexpr int kQueryLead = 4;      // Stage-2 tiles each loader thread keeps in flight
-constexpr int kWideLoaders = 4;    // loader wavefronts of the 32-row Stage-2 kernel
-constexpr int kWideLead = 3;       // tiles each of its loader threads keeps in flight
+constexpr int kQueryLoaders = 4;   // Stage-2 wavefronts that load and rotate the tiles
+constexpr int kQueryLead = 3;      // tiles each of their threads keeps in flight
 constexpr int kMaxHalf = 64;       // head_dim / 2 upper bound (head_dim <= 128)
 
 // RoPE frequencies in revolutions per position: w_i / (2 pi), w_i = theta^(-2i/d),
@@ -131,9 +129,8 @@ struct QueryArgs {
   int32_t n_inline;       // > 0: the table block is `inl` below
   int32_t n_new, hq, hkv, batch;
   int32_t rows;           // n_new * (hq / hkv) packed rows per kv head
-  int32_t wide;           // 0: 16-row wavefronts; 1: 32-row wavefronts
-  int32_t row_waves;      // 16-row: 1, 2 or 4 (each with 2 key halves); 32-row: 2, 3 or 4
-  int32_t row_groups;     // row groups of rows_per_wave * row_waves rows
+  int32_t row_waves;      // 32-row attention wavefronts per workgroup: 1 .. 4
+  int32_t row_groups;     // row groups of 32 * row_waves rows
   int32_t n_split;        // key splits per (batch, kv head, row group)
   int32_t tiles_per_split;
   int64_t cap;

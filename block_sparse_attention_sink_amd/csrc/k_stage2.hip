@@ -16,7 +16,7 @@
 //                                  over a segment list (pool blocks and new
 //                                  tokens are rotated while staged; new tokens
 //                                  are also appended to the context buffer).
-//   k_query_wide_bf16<D, NWA>      the same for more rows: 32-row wavefronts
+//   k_query_bf16<D, NWA>      the same for more rows: 32-row wavefronts
 //                                  on the software-pipelined prefill core.
 //   k_combine                      log-sum-exp merge of the split partials.
 //   k_query_f32                    float32 rows (one wavefront per row).
@@ -139,384 +139,12 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row sources of the 64-key tiles of one split (one row per lane of the
-// planning wavefront): address of the row's K and V (pool, context buffer or
-// new tokens), whether it is rotated (pool rows and new tokens) and whether
-// it is a new token (also written to the context buffer), plus the tile's
-// RoPE angles cos / sin(w_i u0).  Tiles are planned in order, so each lane
-// follows its row's segment forward instead of searching for it; tiles past
-// the context repeat its last row (masked), so their loads stay in bounds.
-// ---------------------------------------------------------------------------
-template <int D, int NT>
-struct TilePlanner {
-  static constexpr uint8_t kRot = 1, kNew = 2;
-  uint64_t kb0, vb0, kb1, vb1, kb2, vb2;
-  int64_t tok0_1, tok0_2;
-  int hkv, g, T, nseg, dst0, it0, s_cur;
-  double fa;
-
-  __device__ __forceinline__ TilePlanner(const QueryArgs& a, int b, int g_, int T_, int nseg_,
-                                         int dst0_,
-                         int it0_, int lane)
-      : kb0(reinterpret_cast<uint64_t>(a.k_pool)), vb0(reinterpret_cast<uint64_t>(a.v_pool)),
-        kb1(reinterpret_cast<uint64_t>(a.k_ctx)), vb1(reinterpret_cast<uint64_t>(a.v_ctx)),
-        kb2(reinterpret_cast<uint64_t>(a.k_new)), vb2(reinterpret_cast<uint64_t>(a.v_new)),
-        tok0_1((int64_t)b * a.cap), tok0_2((int64_t)b * a.n_new), hkv(a.hkv), g(g_), T(T_),
-        nseg(nseg_), dst0(dst0_), it0(it0_), s_cur(-1), fa(a.freq.rev[lane % (D / 2)]) {}
-
-  __device__ __forceinline__ void plan(int li, int lane, const int32_t* seg_start,
-                                       const int32_t* seg_src, const int32_t* seg_buf,
-                                       uint64_t (*row_k)[kKeyTile], uint64_t (*row_v)[kKeyTile],
-                                       uint8_t (*row_flag)[kKeyTile], int32_t (*row_dst)[kKeyTile],
-                                       f32x2 (*rot_a)[kMaxHalf]) {
-    const int u_real = (it0 + li) * kKeyTile + lane;
-    const bool real = u_real < T;
-    const int u = min(u_real, T - 1);
-    if (s_cur < 0) {
-      s_cur = upper_index(seg_start, nseg, u);
-    } else {
-      while (s_cur + 1 < nseg && seg_start[s_cur + 1] <= u) ++s_cur;
-    }
-    const int sg = s_cur;
-    const int64_t tok = seg_src[sg] + (u - seg_start[sg]);
-    const int buf = seg_buf[sg];
-    // Branch-free select of the source (a pointer select here is otherwise
-    // lowered to a lookup table in scratch memory).
-    const uint64_t m0 = buf == 0 ? ~0ull : 0ull, m1 = buf == 1 ? ~0ull : 0ull;
-    const uint64_t m2 = ~(m0 | m1);
-    const int64_t trow = (buf == 0 ? 0 : buf == 1 ? tok0_1 : tok0_2) + tok;
-    const uint64_t off = 2ull * static_cast<uint64_t>((trow * hkv + g) * D);
-    const int slot = li & (NT - 1);
-    row_k[slot][lane] = ((kb0 & m0) | (kb1 & m1) | (kb2 & m2)) + off;
-    row_v[slot][lane] = ((vb0 & m0) | (vb1 & m1) | (vb2 & m2)) + off;
-    row_flag[slot][lane] = real ? (buf != 1 ? kRot : 0) | (buf == 2 ? kNew : 0) : 0;
-    row_dst[slot][lane] = dst0 + (int)tok;
-    if (lane < D / 2) {
-      float c, sn;
-      rope_cs((int64_t)(it0 + li) * kKeyTile, fa, c, sn);
-      rot_a[slot][lane] = f32x2{c, sn};
-    }
-  }
-};
-
-// Rotate one (row, chunk pair) of a K tile at u0 + row: angle(u0 + row) =
-// angle(u0) (tile table ap: cos, sin of 8 frequencies) + angle(row) (row
-// table bp), two frequencies (one 32-bit word of each chunk) at a time.
-__device__ __forceinline__ void rotate_pair(u32x4& x1, u32x4& x2, const f32x4* ap,
-                                            const f32x4* bp) {
-  uint32_t wa[4] = {x1.x, x1.y, x1.z, x1.w}, wb[4] = {x2.x, x2.y, x2.z, x2.w};
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    // Half the angle reads at a time (fewer registers than all eight).
-    if (h == 2) __builtin_amdgcn_sched_barrier(0);
-    const f32x4 av = ap[h], bv = bp[h];
-    float c0, s0, c1, s1;
-    angle_add(av[0], av[1], bv[0], bv[1], c0, s0);
-    angle_add(av[2], av[3], bv[2], bv[3], c1, s1);
-    const float a0 = bf16_lo(wa[h]), a1 = bf16_hi(wa[h]);
-    const float b0 = bf16_lo(wb[h]), b1 = bf16_hi(wb[h]);
-    wa[h] = pack_bf16x2(rot_lo(a0, b0, c0, s0), rot_lo(a1, b1, c1, s1));
-    wb[h] = pack_bf16x2(rot_hi(a0, b0, c0, s0), rot_hi(a1, b1, c1, s1));
-  }
-  x1 = u32x4{wa[0], wa[1], wa[2], wa[3]};
-  x2 = u32x4{wb[0], wb[1], wb[2], wb[3]};
-}
-
-// ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
-// Workgroup = RWW x KSPL attention wavefronts over 16 RWW packed rows (row =
-// token * G + head in group) of one KV head and one key split, plus
-// kQueryLoaders loader wavefronts.  Attention: 16 rows per wavefront on
-// v_mfma_f32_16x16x32_bf16 (see Flash16); with KSPL = 2 the two halves of
-// every 64-key tile go to two wavefronts with their own softmax state,
-// merged through LDS at the end.  Loaders: each thread owns one (row, chunk
-// pair) of every tile; it loads the pair's K and V bytes into registers
-// kLead tiles ahead of use, rotates K at the row's virtual position in
-// registers, and writes both into a two-stage LDS ring (row sources come
-// from a per-tile address table that loader wavefront 0 plans one tile
-// before the loads).  The loads' completion is tracked by the compiler, so
-// each rotation waits for exactly its own tile.  Rows of the new tokens also
-// go to the context buffer (the first row group writes them).
-// ---------------------------------------------------------------------------
-template <int D, int RWW, int KSPL>
-__global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf16(QueryArgs a) {
-  using Gm = TileGeom<D>;
-  constexpr int NWA = RWW * KSPL, NL = kQueryLoaders, NW = NWA + NL, KH = kKeyTile / KSPL;
-  constexpr int KS = D / 32, OT = D / 16, CP = D / 16, CR = D / 8;
-  constexpr int RW = 16;        // rows per wavefront
-  constexpr int NST = 2;        // LDS stages (K + V of one tile each)
-  constexpr int P = kQueryLead;  // tiles in flight per loader thread
-  constexpr int NT = 8;         // address-table slots (>= P + 2)
-  static_assert(NT >= P + 2 && (NT & (NT - 1)) == 0, "table ring");
-  static_assert(CP <= NL, "one (row, chunk pair) per loader thread");
-  constexpr uint8_t kRot = 1, kNew = 2;
-  constexpr int H = D / 2;
-  __shared__ __align__(16) char lds[NST * Gm::STAGE];
-  __shared__ __align__(16) f32x2 rot_a[NT][kMaxHalf];  // cos / sin of w_i * u0 per tile
-  __shared__ __align__(16) f32x2 rot_b[kKeyTile][H];    // cos / sin of w_i * row
-  __shared__ int32_t seg_start[kMaxSegments + 1], seg_src[kMaxSegments], seg_buf[kMaxSegments];
-  __shared__ uint64_t row_k[NT][kKeyTile], row_v[NT][kKeyTile];
-  __shared__ int32_t row_dst[NT][kKeyTile];
-  __shared__ uint8_t row_flag[NT][kKeyTile];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool loader = wave >= NWA;
-  const int ltid = tid - 64 * NWA;  // thread index among the loaders
-  const int rw = wave % RWW, kh = loader ? 0 : wave / RWW;  // row wavefront, key half
-  const int q16 = (lane >> 4) & 3, r16 = lane & 15;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y % a.hkv, rg = blockIdx.y / a.hkv, b = blockIdx.z;
-  const int G = a.hq / a.hkv;
-  const int wrow0 = rg * (RW * RWW) + rw * RW;
-  const bool wave_live = !loader && wrow0 < a.rows;
-  const int rho = wrow0 + r16;
-  const bool live = !loader && rho < a.rows;
-  const int r = live ? rho / G : 0;
-  const int head = g * G + (live ? rho - (rho / G) * G : 0);
-  const int32_t* tab = seg_block(a);
-  const int pos0 = tab[a.seg.o_pos0 + b];
-  const int dst0 = tab[a.seg.o_dst + b];
-  const int qpos = pos0 + r;
-
-  const int nseg = tab[a.seg.o_nseg + b];
-  {
-    const int32_t* st = tab + a.seg.o_start + b * a.seg.stride;
-    const int32_t* sr = tab + a.seg.o_src + b * a.seg.stride;
-    const int32_t* sb = tab + a.seg.o_buf + b * a.seg.stride;
-    for (int i = tid; i <= nseg; i += 64 * NW) {
-      seg_start[i] = st[i];
-      if (i < nseg) {
-        seg_src[i] = sr[i];
-        seg_buf[i] = sb[i];
-      }
-    }
-  }
-
-  bf16x8 qb[KS];
-  {
-    u32x4 raw[KS];
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.n_new + r) * a.hq + head) * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[4 * ks + q16] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], qpos, a.freq, 32 * ks + 8 * q16, a.q_scale);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-  }
-  __syncthreads();  // segment table visible; Q loads retired
-
-  const int T = seg_start[nseg];
-  const int n_tiles = (T + kKeyTile - 1) / kKeyTile;
-  const int it0 = split * a.tiles_per_split;
-  const int cnt = max(0, min(it0 + a.tiles_per_split, n_tiles) - it0);
-
-  if (loader) {
-    TilePlanner<D, NT> tp(a, b, g, T, nseg, dst0, it0, lane);
-    auto plan = [&](int li) {
-      if (wave == NWA) tp.plan(li, lane, seg_start, seg_src, seg_buf, row_k, row_v, row_flag, row_dst, rot_a);
-    };
-
-    // This thread's (row, chunk pair): chunks c and c + CP of one row of
-    // every tile (the two halves RoPE pairs up).  With fewer pairs than
-    // loader threads the rest load a copy and store nothing (loads stay
-    // unconditional, so the compiler's completion counts stay exact).
-    const bool active = kKeyTile * CP == 64 * NL || ltid < kKeyTile * CP;
-    const int item = ltid % (kKeyTile * CP);
-    const int row = item / CP, c = item % CP;
-    const int ko1 = row * Gm::ROW + Gm::k_phys(row, c) * 16;
-    const int ko2 = row * Gm::ROW + Gm::k_phys(row, c + CP) * 16;
-    const int vo1 = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, c) * 16;
-    const int vo2 = Gm::KBYTES + row * Gm::ROW + Gm::v_phys(row, c + CP) * 16;
-    for (int i = ltid; i < kKeyTile * H; i += 64 * NL) {
-      float cb, sb;
-      rope_cs(i / H, a.freq.rev[i % H], cb, sb);
-      rot_b[i / H][i % H] = f32x2{cb, sb};
-    }
-    const bool writer = rg == 0;  // one row group writes the new tokens back
-
-    u32x4 kr[P][2], vr[P][2];
-    auto issue = [&](auto set, int li) {
-      constexpr int S = decltype(set)::value;
-      const int slot = li & (NT - 1);
-      // Global (not flat) loads: flat ones would also count against the LDS
-      // counter that every barrier below waits for.
-      typedef const __attribute__((address_space(1))) u32x4* gptr;
-      const gptr kp = reinterpret_cast<gptr>(row_k[slot][row]);
-      const gptr vp = reinterpret_cast<gptr>(row_v[slot][row]);
-      kr[S][0] = kp[c];
-      kr[S][1] = kp[c + CP];
-      vr[S][0] = vp[c];
-      vr[S][1] = vp[c + CP];
-    };
-    // Rotate tile li's K pair at u0 + row (tile angle + row angle) and store
-    // K and V into the tile's stage; new tokens also go to the context buffer.
-    auto store = [&](auto set, int li) {
-      constexpr int S = decltype(set)::value;
-      if (!active) return;
-      const int slot = li & (NT - 1);
-      char* st = lds + (li % NST) * Gm::STAGE;
-      u32x4 x1 = kr[S][0], x2 = kr[S][1];
-      const uint8_t f = row_flag[slot][row];
-      if (f & kRot) {
-        // (rotate_pair written out: as a call the compiler keeps more of the
-        // angle reads live at once.)
-        const f32x4* ap = reinterpret_cast<const f32x4*>(&rot_a[slot][8 * c]);
-        const f32x4* bp = reinterpret_cast<const f32x4*>(&rot_b[row][8 * c]);
-        uint32_t wa[4] = {x1.x, x1.y, x1.z, x1.w}, wb[4] = {x2.x, x2.y, x2.z, x2.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          if (h == 2) __builtin_amdgcn_sched_barrier(0);
-          const f32x4 av = ap[h], bv = bp[h];
-          float c0, s0, c1, s1;
-          angle_add(av[0], av[1], bv[0], bv[1], c0, s0);
-          angle_add(av[2], av[3], bv[2], bv[3], c1, s1);
-          const float a0 = bf16_lo(wa[h]), a1 = bf16_hi(wa[h]);
-          const float b0 = bf16_lo(wb[h]), b1 = bf16_hi(wb[h]);
-          wa[h] = pack_bf16x2(rot_lo(a0, b0, c0, s0), rot_lo(a1, b1, c1, s1));
-          wb[h] = pack_bf16x2(rot_hi(a0, b0, c0, s0), rot_hi(a1, b1, c1, s1));
-        }
-        x1 = u32x4{wa[0], wa[1], wa[2], wa[3]};
-        x2 = u32x4{wb[0], wb[1], wb[2], wb[3]};
-      }
-      *reinterpret_cast<u32x4*>(st + ko1) = x1;
-      *reinterpret_cast<u32x4*>(st + ko2) = x2;
-      *reinterpret_cast<u32x4*>(st + vo1) = vr[S][0];
-      *reinterpret_cast<u32x4*>(st + vo2) = vr[S][1];
-      if ((f & kNew) && writer) {
-        keep_branch();
-        const int64_t d = (((int64_t)b * a.cap + row_dst[slot][row]) * a.hkv + g) * CR;
-        u32x4* ko = static_cast<u32x4*>(a.k_ctx);
-        u32x4* vo = static_cast<u32x4*>(a.v_ctx);
-        ko[d + c] = x1;
-        ko[d + c + CP] = x2;
-        vo[d + c] = vr[S][0];
-        vo[d + c + CP] = vr[S][1];
-      }
-    };
-
-    // Barriers shared with the attention wavefronts: one after the plans of
-    // tiles 0..P, one after tile 0 is stored, then one per later tile.
-    for (int li = 0; li <= P; ++li) plan(li);
-    waitcnt<0, 0>();
-    barrier_nofence();
-    if (cnt > 0) {
-      static_for<P>([&](auto t) { issue(t, (int)decltype(t)::value); });
-      store(std::integral_constant<int, 0>{}, 0);
-      waitcnt<63, 0>();
-      barrier_nofence();
-    }
-    // Iteration li (the attention uses tile li): request tile li + P into
-    // the register set tile li left, plan tile li + P + 1, store tile li + 1
-    // into the stage tile li - 1 left.  Whole groups of P iterations run
-    // without branches around the loads; the last < P iterations follow.
-    int l0 = 0;
-    for (; l0 + P < cnt; l0 += P) {
-      static_for<P>([&](auto t) {
-        constexpr int S = decltype(t)::value;
-        issue(t, l0 + S + P);
-        plan(l0 + S + P + 1);
-        store(std::integral_constant<int, (S + 1) % P>{}, l0 + S + 1);
-        waitcnt<63, 0>();
-        barrier_nofence();
-      });
-    }
-    static_for<P>([&](auto t) {
-      constexpr int S = decltype(t)::value;
-      if (l0 + S + 1 < cnt) {
-        store(std::integral_constant<int, (S + 1) % P>{}, l0 + S + 1);
-        waitcnt<63, 0>();
-        barrier_nofence();
-      }
-    });
-    if constexpr (KSPL == 2) {  // the attention wavefronts' merge below
-      __syncthreads();
-      __syncthreads();
-    }
-    return;
-  }
-
-  Flash16<D> fl;
-  fl.init();
-  int koff[KS], vbase[OT];
-  lane_offsets16<D>(lane, kh * KH, koff, vbase);
-  waitcnt<0, 0>();
-  barrier_nofence();
-  for (int li = 0; li < cnt; ++li) {
-    waitcnt<0, 0>();  // this wavefront's reads of tile li-1 are done
-    barrier_nofence();
-    if (wave_live) {
-      const int k0 = (it0 + li) * kKeyTile + kh * KH;
-      const int lim = qpos - k0;  // keys kr <= lim are visible (causal over new tokens)
-      fl.template tile<KH>(lds + (li % NST) * Gm::STAGE, koff, vbase, qb, k0 + KH - 1 > pos0,
-                           [=](int kr) { return kr <= lim; });
-    }
-  }
-  (void)CR;
-
-  float lsum = fl.total();
-  if constexpr (KSPL == 2) {
-    // Second key half -> LDS (the ring is free once every wavefront is past
-    // its last tile); the first half merges: weights 2^(m_h - M) over halves
-    // that saw a key.
-    __syncthreads();
-    float* xo = reinterpret_cast<float*>(lds) + rw * (OT * 256 + 32);
-    if (kh == 1) {
-#pragma unroll
-      for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4*>(xo + (t * 64 + lane) * 4) = fl.o[t];
-      if (q16 == 0) {
-        xo[OT * 256 + 2 * r16] = fl.m;
-        xo[OT * 256 + 2 * r16 + 1] = lsum;
-      }
-    }
-    __syncthreads();
-    if (kh == 1) return;
-    const float m1 = xo[OT * 256 + 2 * r16], l1 = xo[OT * 256 + 2 * r16 + 1];
-    const bool h0 = lsum > 0.0f, h1 = l1 > 0.0f;
-    const float M = h0 && h1 ? fmaxf(fl.m, m1) : h1 ? m1 : fl.m;
-    const float w0 = h0 ? __builtin_amdgcn_exp2f(fl.m - M) : 0.0f;
-    const float w1 = h1 ? __builtin_amdgcn_exp2f(m1 - M) : 0.0f;
-#pragma unroll
-    for (int t = 0; t < OT; ++t) {
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + (t * 64 + lane) * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fl.o[t][i] = w0 * fl.o[t][i] + w1 * o1[i];
-    }
-    fl.m = M;
-    lsum = w0 * lsum + w1 * l1;
-  }
-  if (!live) return;
-  if (a.n_split == 1) {
-    const float inv = 1.0f / lsum;
-    uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
-#pragma unroll
-    for (int t = 0; t < OT; ++t) {
-      const int d = 16 * t + 4 * q16;
-      const u32x2 w = {pack_bf16x2(fl.o[t][0] * inv, fl.o[t][1] * inv),
-                       pack_bf16x2(fl.o[t][2] * inv, fl.o[t][3] * inv)};
-      *reinterpret_cast<u32x2*>(op + d) = w;
-    }
-  } else {
-    const int64_t prow = (((int64_t)b * a.hkv + g) * a.n_split + split) * a.rows + rho;
-    float* po = a.part_o + prow * D;
-#pragma unroll
-    for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t + 4 * q16) = fl.o[t];
-    if (q16 == 0) {
-      a.part_ml[prow * 2 + 0] = fl.m;
-      a.part_ml[prow * 2 + 1] = lsum;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Query attention for many packed rows (GQA groups times query tokens), bf16
-// MFMA, split-K over the context.
-//
-// Workgroup = NWA attention wavefronts of 32 packed rows each (the software-
+// Rows = (query token, head in GQA group) packed per KV head.  Workgroup =
+// NWA attention wavefronts of 32 packed rows each (the software-
 // pipelined Flash core of the prefill, on v_mfma_f32_32x32x16_bf16) plus
-// kWideLoaders loader wavefronts, one of each kind per SIMD: a 32-row
+// kQueryLoaders loader wavefronts, one of each kind per SIMD: a 32-row
 // attention wavefront needs half of a SIMD's registers.  Iteration i of the
 // attention computes the softmax of tile i, P V of tile i - 1 and the scores
 // of tile i + 1, so it reads K of tile i + 1 and V of tile i - 1; meanwhile
@@ -530,11 +158,11 @@ __global__ __launch_bounds__(64 * (RWW * KSPL + kQueryLoaders)) void k_query_bf1
 // (their rotated K and their V) also go to the context buffer.
 // ---------------------------------------------------------------------------
 template <int D, int NWA>
-__global__ __launch_bounds__(64 * (NWA + kWideLoaders), 1) void k_query_wide_bf16(QueryArgs a) {
+__global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
-  constexpr int NL = kWideLoaders, NW = NWA + NL;
+  constexpr int NL = kQueryLoaders, NW = NWA + NL;
   constexpr int KS = D / 16, OT = D / 32, CP = D / 16, CR = D / 8, H = D / 2;
-  constexpr int P = kWideLead;
+  constexpr int P = kQueryLead;
   constexpr int NT = 8;  // tile-angle table slots
   static_assert(NT >= P + 2 && (NT & (NT - 1)) == 0, "angle table ring");
   constexpr int ITEMS = kKeyTile * CP / (64 * NL);  // (row, chunk pair) items per loader thread
@@ -1012,20 +640,13 @@ hipError_t launch_new_kv(const NewKVArgs& a, int batch, int head_dim, int dtype,
 
 template <int D>
 static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.wide) {
-    const int w = a.n_split * a.hkv * grid.z;
-    grid = dim3(a.row_groups > 1 ? (w + 7) / 8 * 8 * a.row_groups : w);
-    switch (a.row_waves) {
-      case 2: hipLaunchKernelGGL((k_query_wide_bf16<D, 2>), grid, dim3(64 * (2 + kWideLoaders)), 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((k_query_wide_bf16<D, 3>), grid, dim3(64 * (3 + kWideLoaders)), 0, stream, a); break;
-      default: hipLaunchKernelGGL((k_query_wide_bf16<D, 4>), grid, dim3(64 * (4 + kWideLoaders)), 0, stream, a); break;
-    }
-    return;
-  }
+  const int w = a.n_split * a.hkv * grid.z;
+  grid = dim3(a.row_groups > 1 ? (w + 7) / 8 * 8 * a.row_groups : w);
   switch (a.row_waves) {
-    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(64 * (2 + kQueryLoaders)), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(64 * (4 + kQueryLoaders)), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_query_bf16<D, 4, 2>), grid, dim3(64 * (8 + kQueryLoaders)), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1>), grid, dim3(64 * (1 + kQueryLoaders)), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2>), grid, dim3(64 * (2 + kQueryLoaders)), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_query_bf16<D, 3>), grid, dim3(64 * (3 + kQueryLoaders)), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_query_bf16<D, 4>), grid, dim3(64 * (4 + kQueryLoaders)), 0, stream, a); break;
   }
 }
 
@@ -1037,9 +658,7 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     else hipLaunchKernelGGL(k_query_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const bool ok = a.wide ? a.row_waves >= 2 && a.row_waves <= 4
-                        : a.row_waves == 1 || a.row_waves == 2 || a.row_waves == 4;
-  if (!ok) return hipErrorInvalidValue;
+  if (a.row_waves < 1 || a.row_waves > 4) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
   if (head_dim == 128) launch_query_d<128>(a, grid, stream);
   else launch_query_d<64>(a, grid, stream);
