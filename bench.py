@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-op", choices=["prefill", "gather", "query", "fused", "copy"],
                     help="run only this operation --steps times (for rocprofv3); prints timing")
+    ap.add_argument("--profile-workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload of --profile-op prefill / fused (4: one layer of the pool)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="time every operation of the five workloads (one JSON line each)")
     args = ap.parse_args()
@@ -125,6 +127,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.all_workloads:
         run_all_workloads(dev)
+        return
+    if args.profile_op in ("prefill", "fused") and args.profile_workload != 2:
+        profile_workload_op(dev, args.profile_op, args.profile_workload, args.steps, args.warmup)
         return
     w = workload(2)
     lens, sink, j, theta = w.block_lens, w.sink, w.j, w.theta
@@ -320,6 +325,47 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def profile_workload_op(dev, op, k, steps, warmup):
+    """Run one hot-path operation of workload k `steps` times (for rocprofv3):
+    the prefill of its pool, or the fused gather + query of its batch (one
+    layer)."""
+    import torch
+    from block_sparse_attention_sink_amd import dbsa
+    from block_sparse_attention_sink_amd.inputs import randn, workload
+
+    w = workload(k)
+    n, hq, hkv, d, dt = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype
+    kk = randn((n, hkv, d), 12, dt, dev)
+    vv = randn((n, hkv, d), 13, dt, dev)
+    if op == "prefill":
+        q = randn((n, hq, d), 11, dt, dev)
+        o = torch.empty_like(q)
+        fn = lambda: dbsa.dbsa_prefill(q, kk, vv, w.block_lens, w.sink, w.j, w.theta, out=o)
+    else:
+        if w.n_new == 0:
+            raise SystemExit(f"workload {k} has no Stage-2 queries")
+        b, nn = w.batch, w.n_new
+        qn = randn((b, nn, hq, d), 21, dt, dev)
+        kn = randn((b, nn, hkv, d), 22, dt, dev)
+        vn = randn((b, nn, hkv, d), 23, dt, dev)
+        on = torch.empty_like(qn)
+        kt = torch.empty((b, nn, hkv, d), dtype=qn.dtype, device=dev)
+        vt = torch.empty_like(kt)
+        fn = lambda: dbsa.dbsa_query_attn_gathered(qn, kn, vn, kk, vv, w.block_lens, w.ids, kt,
+                                                   vt, [0] * b, w.theta, out=on)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(steps):
+        fn()
+    a1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_op": op, "workload": w.name, "steps": steps,
+                      "ms_per_call": a0.elapsed_time(a1) / steps}))
 
 
 def run_all_workloads(dev):

@@ -224,8 +224,11 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
       return;
     }
     // Item k of this thread: row ltid / CP + k * 64 / ITEMS, chunks c and
-    // c + CP (the two halves RoPE pairs up).
+    // c + CP (the two halves RoPE pairs up).  Rows past the split's last
+    // key (the look-ahead past its last tile) repeat that key: they are
+    // never used, and so cost no traffic beyond the split's own keys.
     const int c = ltid % CP;
+    const int tend = min(T, (it0 + cnt) * kKeyTile);
     const uint64_t kb0 = reinterpret_cast<uint64_t>(a.k_pool), vb0 = reinterpret_cast<uint64_t>(a.v_pool);
     const uint64_t kb1 = reinterpret_cast<uint64_t>(a.k_ctx), vb1 = reinterpret_cast<uint64_t>(a.v_ctx);
     const uint64_t kb2 = reinterpret_cast<uint64_t>(a.k_new), vb2 = reinterpret_cast<uint64_t>(a.v_new);
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
       ko2[k] = row * Gm::ROW + Gm::k_phys(row, c + CP) * 16;
       vo1[k] = row * Gm::ROW + Gm::v_phys(row, c) * 16;
       vo2[k] = row * Gm::ROW + Gm::v_phys(row, c + CP) * 16;
-      enter(kk, upper_index(seg_start, nseg, min(it0 * kKeyTile + row, T - 1)));
+      enter(kk, upper_index(seg_start, nseg, min(it0 * kKeyTile + row, tend - 1)));
 #pragma unroll
       for (int i = 0; i < 8; ++i) rope_cs(row, a.freq.rev[8 * c + i], rb_c[k][i], rb_s[k][i]);
     });
@@ -274,15 +277,15 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     typedef const __attribute__((address_space(1))) u32x4* gptr;  // global, not flat, loads
     u32x4 kr[P][ITEMS][2], vr[P][ITEMS][2];
     int fl[P][ITEMS];  // per tile and item: 4 * context-buffer row + (new << 1) + rotate
-    // Loads of tile t into register set S (tiles past the split repeat the
-    // context's last row, so the loads never need a branch); the first
+    // Loads of tile t into register set S (tiles past the split repeat its
+    // last row, so the loads never need a branch); the first
     // loader wavefront also writes the tile's angles.
     auto issue = [&](auto set, int t) __attribute__((always_inline)) {
       constexpr int S = decltype(set)::value;
       static_for<ITEMS>([&](auto kk) __attribute__((always_inline)) {
         constexpr int k = decltype(kk)::value;
         const int u_real = (it0 + t) * kKeyTile + rows[k];
-        const int u = min(u_real, T - 1);
+        const int u = min(u_real, tend - 1);
         while (u >= send[k]) enter(kk, sidx[k] + 1);
         const uint64_t ka = kaddr0[k] + static_cast<uint64_t>((int64_t)u * rstride);
         const gptr kp = reinterpret_cast<gptr>(ka);
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
         kr[S][k][1] = kp[c + CP];
         vr[S][k][0] = vp[c];
         vr[S][k][1] = vp[c + CP];
-        fl[S][k] = u_real < T ? (int)((uint32_t)fbase[k] + ((uint32_t)u << 2)) : 0;
+        fl[S][k] = u_real < tend ? (int)((uint32_t)fbase[k] + ((uint32_t)u << 2)) : 0;
       });
       if (wave == NWA && lane < H) {
         float cs, sn;

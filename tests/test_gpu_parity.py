@@ -242,7 +242,7 @@ def test_query_attn_gqa_many_rows_and_split():
         _stage2_case("bf16", 16, 4, 128, lens, ids, 64, 5e5, 111, fused)
 
 
-def test_query_wide_rows_head_dim_64_and_three_waves():
+def test_query_many_rows_head_dim_64_and_three_waves():
     """Many packed rows per KV head on the 32-row kernels: head_dim 64 with
     two row groups of 80 rows (3 wavefronts each), and head_dim 128 with 76
     rows in one group; both fused and materialised, split and unsplit."""
