@@ -151,7 +151,7 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 // the loaders store K and V of tile i + 2 (K ring of two LDS stages, V ring
 // of four).  Each loader thread owns two (row, chunk pair) items of every
 // tile: it follows its rows through the segment list in registers, keeps
-// every tile's K and V in registers kLead tiles ahead of its store (the
+// every tile's K and V in registers kQueryLead tiles ahead of its store (the
 // compiler counts these loads, so every store waits for exactly its own
 // tile) and rotates K at the row's virtual position on the way to LDS (row
 // angles in registers, the tile's angles from a small table).  New tokens
@@ -179,8 +179,8 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
   // Work item (split, KV head g, row group rg, batch row b).  With several
   // row groups, those of one (split, head, batch row) take consecutive
   // workgroup slots of one XCD (ids 8 apart: the hardware deals consecutive
-  // ids to the 8 XCDs in turn), so they run side by side and the second
-  // load of every tile hits that XCD's L2 instead of HBM.
+  // ids to the 8 XCDs in turn), so they run side by side and can share the
+  // tile reads through that XCD's L2.
   const int R = a.row_groups, W = a.n_split * a.hkv * a.batch;
   const int lin = blockIdx.x;
   const int rg = R > 1 ? (lin >> 3) % R : 0;
