@@ -480,6 +480,20 @@ __device__ __forceinline__ void dma16(const void* gsrc, const void* lds_dst) {
       : "memory");
 }
 
+// The same with a wave-uniform base address (in scalar registers) and a
+// 32-bit per-lane byte offset: the per-lane 64-bit address arithmetic of
+// dma16 disappears when the offsets stay fixed across tiles.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, const void* lds_dst) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)lds_dst));
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "{m0}"(base)
+      : "memory");
+}
+
 __device__ __forceinline__ void copy_to_lds(const u32x4* src, char* dst, int chunks, int wave,
                                             int nw, int lane) {
   for (int i = wave; i * 64 < chunks; i += nw) dma16(src + i * 64 + lane, dst + i * 1024);

@@ -142,7 +142,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     char* st = kring + (it % NS) * Gm::KBYTES;
     const u32x4* kt = kbase + (int64_t)slot_of(tile_of(it)) * Gm::TU4;
 #pragma unroll
-    for (int jj = 0; jj < NPW; ++jj) dma16(kt + kl[jj], st + (wsc + jj * kPrefillWaves) * 1024);
+    for (int jj = 0; jj < NPW; ++jj)
+      dma16s(16u * kl[jj], kt, st + (wsc + jj * kPrefillWaves) * 1024);
   };
   auto load_v = [&](int it) {
     char* st = vring + (it % NS) * Gm::VBYTES;
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     if ((kt + 1) * kKeyTile <= a.n_keys) {
       const uint16_t* vt = vsrc + kt * vtile;
 #pragma unroll
-      for (int jj = 0; jj < NPW; ++jj) dma16(vt + vo[jj], st + (wsc + jj * kPrefillWaves) * 1024);
+      for (int jj = 0; jj < NPW; ++jj)
+        dma16s(2u * vo[jj], vt, st + (wsc + jj * kPrefillWaves) * 1024);
     } else {  // last, partial key tile: rows past the keys repeat the last key (masked)
 #pragma unroll
       for (int jj = 0; jj < NPW; ++jj) {
