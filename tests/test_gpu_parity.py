@@ -257,6 +257,18 @@ def test_query_many_rows_head_dim_64_and_three_waves():
                  195, True)
 
 
+def test_query_odd_head_count_pads_the_grid():
+    """3 KV heads x 4-head groups x 48 tokens = 192 rows in two row groups: the
+    (split, head) work items are not a multiple of 8, so the grid carries
+    padding slots that must exit cleanly."""
+    rng = np.random.default_rng(47)
+    lens = rng.integers(200, 900, size=9).astype(np.int32)
+    ids = np.array([[0, 2, 5, 8]], np.int32)
+    for fused in (False, True):
+        _stage2_case("bf16", 12, 3, 128, lens, ids, 48, 5e5, 201, fused)
+        _stage2_case("bf16", 12, 3, 64, lens, ids, 7, 1e4, 203, fused)
+
+
 def test_query_fused_equals_materialised_bitwise():
     rng = np.random.default_rng(23)
     lens = rng.integers(50, 700, size=12).astype(np.int32)
