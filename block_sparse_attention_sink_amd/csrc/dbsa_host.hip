@@ -225,10 +225,12 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
 
 int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Plan& p,
                   const void* q, int32_t q_row0, const void* k, const void* v, void* o,
-                  void* ws, hipStream_t s) {
+                  void* ws, hipStream_t s, bool stage_table = true) {
   char* w = static_cast<char*>(ws);
-  int rc = stage_bytes(p.off.data(), p.meta_bytes, w + p.off_meta, s);
-  if (rc) return rc;
+  if (stage_table) {  // (layers after the first reuse the table already staged)
+    const int rc = stage_bytes(p.off.data(), p.meta_bytes, w + p.off_meta, s);
+    if (rc) return rc;
+  }
   const RopeFreq freq = make_freq(a);
   PrefillArgs pa;
   pa.q = q;
@@ -581,6 +583,45 @@ int dbsa_prefill(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, const voi
   if (!rc) rc = check_ws(ws, ws_bytes, p.total);
   if (rc) return rc;
   return launch_stage1(attn, blocks, p, q, 0, k, v, o, ws, static_cast<hipStream_t>(stream));
+}
+
+int dbsa_prefill_layers(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, int32_t n_layers,
+                        const void* q, int64_t q_layer_stride, const void* k, const void* v,
+                        int64_t kv_layer_stride, void* o, int64_t o_layer_stride, void* ws,
+                        size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  Stage1Plan p;
+  int rc = plan_prefill(attn, blocks, p);
+  if (!rc) rc = check_ptrs({q, k, v, o}, "q, k, v, o");
+  if (!rc) rc = check_ws(ws, ws_bytes, p.total);
+  if (rc) return rc;
+  if (n_layers < 1) return fail(DBSA_EINVAL, "n_layers must be >= 1");
+  const int64_t eb = elem_bytes(attn);
+  const int64_t q_extent = (int64_t)p.n_tokens * attn->n_q_heads * attn->head_dim;
+  const int64_t kv_extent = (int64_t)p.n_tokens * attn->n_kv_heads * attn->head_dim;
+  if (n_layers > 1) {
+    if (o_layer_stride < q_extent)
+      return fail(DBSA_EINVAL, "o_layer_stride %lld is below one layer of o (%lld elements)",
+                  (long long)o_layer_stride, (long long)q_extent);
+    if (q_layer_stride != 0 && q_layer_stride < q_extent)
+      return fail(DBSA_EINVAL, "q_layer_stride must be 0 or >= %lld elements",
+                  (long long)q_extent);
+    if (kv_layer_stride != 0 && kv_layer_stride < kv_extent)
+      return fail(DBSA_EINVAL, "kv_layer_stride must be 0 or >= %lld elements",
+                  (long long)kv_extent);
+    if ((q_layer_stride * eb) % 16 || (kv_layer_stride * eb) % 16 || (o_layer_stride * eb) % 16)
+      return fail(DBSA_EINVAL, "layer strides must be multiples of 16 bytes");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const char* ql = static_cast<const char*>(q) + l * q_layer_stride * eb;
+    const char* kl = static_cast<const char*>(k) + l * kv_layer_stride * eb;
+    const char* vl = static_cast<const char*>(v) + l * kv_layer_stride * eb;
+    char* ol = static_cast<char*>(o) + l * o_layer_stride * eb;
+    rc = launch_stage1(attn, blocks, p, ql, 0, kl, vl, ol, ws, s, l == 0);
+    if (rc) return rc;
+  }
+  return DBSA_OK;
 }
 
 int dbsa_append_block(const dbsa_attn_t* attn, const dbsa_blocks_t* existing, int32_t new_len,

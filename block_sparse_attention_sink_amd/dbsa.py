@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "DbsaError", "load", "dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope",
+    "DbsaError", "load", "dbsa_prefill", "dbsa_prefill_layers", "dbsa_append_block",
+    "dbsa_gather_rope",
     "dbsa_query_attn", "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_version",
     "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "OP_GATHER_SPANS",
     "OP_QUERY_SPANS", "SYMBOLS", "dbsa_gather_rope_spans", "dbsa_query_attn_spans", "llama31_inv_freq",
@@ -26,7 +27,7 @@ OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 OP_PREFILL, OP_APPEND, OP_GATHER, OP_QUERY, OP_QUERY_GATHERED = 0, 1, 2, 3, 4
 OP_GATHER_SPANS, OP_QUERY_SPANS = 5, 6
-SYMBOLS = ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
+SYMBOLS = ("dbsa_prefill", "dbsa_prefill_layers", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
            "dbsa_query_attn_gathered", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
            "dbsa_workspace_bytes", "dbsa_last_error", "dbsa_version")
 
@@ -65,6 +66,7 @@ def load() -> ctypes.CDLL:
     pa, pb = ctypes.POINTER(AttnT), ctypes.POINTER(BlocksT)
     p32, p64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.dbsa_prefill.argtypes = [pa, pb, vp, vp, vp, vp, vp, sz, vp]
+    lib.dbsa_prefill_layers.argtypes = [pa, pb, i32, vp, i64, vp, vp, i64, vp, i64, vp, sz, vp]
     lib.dbsa_append_block.argtypes = [pa, pb, i32, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
     lib.dbsa_gather_rope.argtypes = [pa, pb, p32, i32, i32, vp, vp, vp, vp, i64, p64, vp, sz, vp]
     lib.dbsa_query_attn.argtypes = [pa, i32, i32, vp, vp, vp, vp, vp, p64, i64, vp, vp, sz, vp]
@@ -218,6 +220,40 @@ def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=
     _check(lib.dbsa_prefill(ctypes.byref(a), ctypes.byref(b.t), _ptr(q, "q"),
                             _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), _ptr(out, "out", q.dtype),
                             _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    return out
+
+
+def dbsa_prefill_layers(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=None):
+    """Stage-1 prefill of every layer: q [L, N, Hq, d] (or [N, Hq, d], shared
+    by all layers), k, v [L, N, Hkv, d] (or [N, Hkv, d], shared); returns O
+    [L, N, Hq, d]."""
+    import torch
+    lib = load()
+    n_layers = max(t.shape[0] if t.dim() == 4 else 1 for t in (q, k, v))
+    ql = q if q.dim() == 4 else q.unsqueeze(0)
+    kl = k if k.dim() == 4 else k.unsqueeze(0)
+    vl = v if v.dim() == 4 else v.unsqueeze(0)
+    _, n, hq, d = ql.shape
+    hkv = kl.shape[2]
+    for name, t in (("q", ql), ("k", kl), ("v", vl)):
+        if t.shape[0] not in (1, n_layers) or not t.is_contiguous():
+            raise DbsaError(EINVAL, f"{name}: {n_layers} layers (or one shared), contiguous")
+    if kl.shape[0] != vl.shape[0]:
+        raise DbsaError(EINVAL, "k and v must have the same number of layers")
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    b = Blocks(block_lens, sink, j)
+    if out is None:
+        out = torch.empty((n_layers, n, hq, d), dtype=q.dtype, device=q.device)
+    stride = lambda t: 0 if t.shape[0] == 1 else t[0].numel()
+    need = lib.dbsa_workspace_bytes(OP_PREFILL, ctypes.byref(a), ctypes.byref(b.t), 0, 1, 0, 0)
+    if need == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    ws = _workspace(need, q.device)
+    _check(lib.dbsa_prefill_layers(
+        ctypes.byref(a), ctypes.byref(b.t), n_layers, _ptr(ql, "q"), stride(ql),
+        _ptr(kl, "k", q.dtype), _ptr(vl, "v", q.dtype), stride(kl), _ptr(out, "out", q.dtype),
+        out[0].numel(), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
     return out
 
 

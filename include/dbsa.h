@@ -107,6 +107,22 @@ int dbsa_prefill(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
                  const void* q, const void* k, const void* v, void* o,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Stage 1 over the layers of a model, one after another on one stream (the
+ * one-time setup of a multi-layer pool, [Notes, Method > Stage 1] per layer;
+ * the pages report its cost against inference in [Notes, Experiments >
+ * efficiency comparison, relative-latency table]).  Layer l reads q + l * q_layer_stride, k + l * kv_layer_stride,
+ * v + l * kv_layer_stride and writes o + l * o_layer_stride (strides in
+ * elements of attn->dtype), each laid out as for dbsa_prefill.  One block
+ * plan serves every layer; the workspace is that of one dbsa_prefill call
+ * (layers reuse it in stream order).  n_layers >= 1.  With n_layers > 1,
+ * o_layer_stride must cover a layer of o, and each input stride must be 0
+ * (every layer reads the same tensor) or cover a layer of that input; every
+ * layer's pointers must be 16-byte aligned.  Errors as dbsa_prefill. */
+int dbsa_prefill_layers(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks, int32_t n_layers,
+                        const void* q, int64_t q_layer_stride, const void* k, const void* v,
+                        int64_t kv_layer_stride, void* o, int64_t o_layer_stride, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Stage 1, incremental: encode one new block onto an existing pool
  * [Notes, Method > Stage 1, item 4; Highlights: constant cost per new block].
  *   existing: the pool's blocks (its N tokens are k_cache/v_cache[0, N)).

@@ -78,6 +78,26 @@ def test_prefill_validation(lib):
     assert _prefill(lib, _attn(), big) == dbsa.EINVAL
 
 
+def test_prefill_layers_validation(lib):
+    blocks = dbsa.Blocks([5, 7, 9], 1, 2)
+    a = _attn()
+    q_ext, kv_ext = 21 * 4 * 128, 21 * 2 * 128
+
+    def call(n, qs, kvs, os_):
+        return lib.dbsa_prefill_layers(ctypes.byref(a), ctypes.byref(blocks.t), n, FAKE, qs, FAKE,
+                                       FAKE, kvs, FAKE, os_, FAKE, 1 << 40, None)
+    assert call(0, q_ext, kv_ext, q_ext) == dbsa.EINVAL
+    assert "n_layers" in _err(lib)
+    assert call(2, q_ext, kv_ext, q_ext - 8) == dbsa.EINVAL  # outputs would overlap
+    assert call(2, q_ext - 8, kv_ext, q_ext) == dbsa.EINVAL
+    assert call(2, q_ext, kv_ext // 2, q_ext) == dbsa.EINVAL
+    assert call(2, q_ext + 4, kv_ext, q_ext) == dbsa.EINVAL  # 8 bytes: misaligned layers
+    assert "16 bytes" in _err(lib)
+    # shared inputs (stride 0) and a single layer with any stride pass the checks
+    assert call(3, 0, 0, q_ext) not in (dbsa.EINVAL, dbsa.EUNSUPPORTED)
+    assert call(1, 3, 5, 7) not in (dbsa.EINVAL, dbsa.EUNSUPPORTED)
+
+
 def test_rope_table_validation_and_llama31_helper(lib):
     ok_blocks = dbsa.Blocks([5, 7, 9], 1, 2)
     table = dbsa.llama31_inv_freq(5e5, 128)

@@ -75,6 +75,31 @@ def test_prefill_f32_tiny_workload():
     assert_close(got, want, "f32", "prefill f32")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_layers_equals_per_layer(dtype):
+    """Three layers through one dbsa_prefill_layers call give, bitwise, what
+    three dbsa_prefill calls give; a shared Q (stride 0) as well."""
+    rng = np.random.default_rng(53)
+    lens = rng.integers(30, 400, size=6).astype(np.int32)
+    n = int(lens.sum())
+    hq, hkv, d = (8, 2, 128) if dtype == "bf16" else (2, 1, 64)
+    q = randn((3, n, hq, d), 211, dtype, DEV)
+    k = randn((3, n, hkv, d), 212, dtype, DEV)
+    v = randn((3, n, hkv, d), 213, dtype, DEV)
+    o = dbsa.dbsa_prefill_layers(q, k, v, lens, 1, 2, 5e5)
+    o_shared = dbsa.dbsa_prefill_layers(q[1].contiguous(), k, v, lens, 1, 2, 5e5)
+    for l in range(3):
+        ol = dbsa.dbsa_prefill(q[l].contiguous(), k[l].contiguous(), v[l].contiguous(), lens, 1,
+                               2, 5e5)
+        os_ = dbsa.dbsa_prefill(q[1].contiguous(), k[l].contiguous(), v[l].contiguous(), lens, 1,
+                                2, 5e5)
+        torch.cuda.synchronize()
+        assert torch.equal(o[l], ol), l
+        assert torch.equal(o_shared[l], os_), l
+    want = orc.prefill(host64(q[2]), host64(k[2]), host64(v[2]), lens, 1, 2, 5e5)
+    assert_close(host64(o[2]), want, dtype, "layer 2")
+
+
 def test_prefill_mask_probe_exact_fractions():
     """Q = 0, V = one-hot(block): every output is (#visible keys of block b) / |vis(t)|.
 
