@@ -11,13 +11,13 @@
 //   k_new_kv_f32                   rotate the new tokens' K at their positions
 //                                  and append K/V to the row's context buffer
 //                                  (float32 path; bf16 does it in k_query_bf16).
-//   k_query_bf16<D, RWW, KSPL>     split-K flash attention of up to 64 packed
+//   k_query_bf16<D, NWA>           split-K flash attention of the packed
 //                                  (token, head-in-group) rows of one KV head
-//                                  over a segment list (pool blocks and new
-//                                  tokens are rotated while staged; new tokens
-//                                  are also appended to the context buffer).
-//   k_query_bf16<D, NWA>      the same for more rows: 32-row wavefronts
-//                                  on the software-pipelined prefill core.
+//                                  over a segment list, 32 rows per attention
+//                                  wavefront on the software-pipelined prefill
+//                                  core (pool blocks and new tokens are rotated
+//                                  while staged; new tokens are also appended
+//                                  to the context buffer).
 //   k_combine                      log-sum-exp merge of the split partials.
 //   k_query_f32                    float32 rows (one wavefront per row).
 #include "dbsa_device.hpp"
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     u32x4 kr[P][ITEMS][2], vr[P][ITEMS][2];
     int fl[P][ITEMS];  // per tile and item: 4 * context-buffer row + (new << 1) + rotate
     // Loads of tile t into register set S (tiles past the split repeat its
-    // last row, so the loads never need a branch); the first
-    // loader wavefront also writes the tile's angles.
+    // last row, so the loads never need a branch); the first loader
+    // wavefront also writes the tile's angles.
     auto issue = [&](auto set, int t) __attribute__((always_inline)) {
       constexpr int S = decltype(set)::value;
       static_for<ITEMS>([&](auto kk) __attribute__((always_inline)) {
