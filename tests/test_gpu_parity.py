@@ -458,3 +458,36 @@ def test_example_level_many_short_spans():
     src, ln = src.astype(np.int32), ln.astype(np.int32)
     o_mat, o_fused = _span_case("bf16", 8, 2, 128, n_pool, src, ln, 6, 5e5, 181)
     assert torch.equal(o_mat, o_fused)
+
+
+def test_spans_with_table_head_dim_64_and_decode():
+    """Example-level spans combined with a RoPE frequency table (head_dim 64,
+    bf16), then decode steps over the same spans with a growing tail buffer."""
+    rng = np.random.default_rng(59)
+    n_pool = 2500
+    src, ln = _demo_spans(rng, n_pool, 40, 2, 7, 5, 90)
+    table = dbsa.llama31_inv_freq(5e5, 64)
+    _span_case("bf16", 8, 2, 64, n_pool, src, ln, 9, table, 221)
+    # query tokens then single-token steps, each appending to the tail
+    hq, hkv, d, theta = 8, 2, 128, 5e5
+    kp = randn((n_pool, hkv, d), 231, "bf16", DEV)
+    vp = randn((n_pool, hkv, d), 232, "bf16", DEV)
+    n_q, steps = 6, 3
+    q = randn((1, n_q + steps, hq, d), 233, "bf16", DEV)
+    kn = randn((1, n_q + steps, hkv, d), 234, "bf16", DEV)
+    vn = randn((1, n_q + steps, hkv, d), 235, "bf16", DEV)
+    tk = torch.zeros((1, n_q + steps, hkv, d), dtype=torch.bfloat16, device=DEV)
+    tv = torch.zeros_like(tk)
+    outs = [dbsa.dbsa_query_attn_spans(q[:, :n_q].contiguous(), kn[:, :n_q].contiguous(),
+                                       vn[:, :n_q].contiguous(), kp, vp, src[:1], ln[:1], tk, tv,
+                                       [0], theta)]
+    for s_ in range(steps):
+        sl = slice(n_q + s_, n_q + s_ + 1)
+        outs.append(dbsa.dbsa_query_attn_spans(q[:, sl].contiguous(), kn[:, sl].contiguous(),
+                                               vn[:, sl].contiguous(), kp, vp, src[:1], ln[:1],
+                                               tk, tv, [n_q + s_], theta))
+    torch.cuda.synchronize()
+    kg, vg = orc.gather_rope_spans(host64(kp), host64(vp), src[0], ln[0], theta)
+    want, _, _ = orc.query_attn(host64(q[0]), host64(kn[0]), host64(vn[0]), kg, vg, theta)
+    got = np.concatenate([host64(o[0]) for o in outs])
+    assert_close(got, want, "bf16", "span query + decode steps")
