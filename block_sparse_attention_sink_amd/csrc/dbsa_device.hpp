@@ -204,6 +204,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedTrans = 0x400;
 
+// A 16-float MFMA accumulator with every element x, written as eight 64-bit
+// moves (the per-element form costs twice the vector instructions).
+__device__ __forceinline__ f32x16 splat16(float x) {
+  typedef double f64x8 __attribute__((ext_vector_type(8)));
+  const double d = __builtin_bit_cast(double, f32x2{x, x});
+  const f64x8 v = {d, d, d, d, d, d, d, d};
+  return __builtin_bit_cast(f32x16, v);
+}
+
 // The vector work of one tile (mask, maximum, exponentials, packing, row sum)
 // is a chain of dependent instructions whose latency a single wavefront cannot
 // hide; the tile loop therefore interleaves it, instruction group by group,
@@ -374,8 +383,7 @@ struct Flash {
       ka[b][0] = kfrag(st_k, koff, (2 * x) % KS, h);
       ka[b][1] = kfrag(st_k, koff, (2 * x + 1) % KS, h);
     };
-#pragma unroll
-    for (int i = 0; i < 16; ++i) n1[i] = -m;
+    n1 = splat16(-m);
     kread(0, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -383,8 +391,7 @@ struct Flash {
       const bool second = x >= H;
       if (x + 1 < KS) kread(x + 1, x + 1 >= H ? 0 : 1, (x + 1) & 1);
       if (x == H) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) n0[i] = -m;
+        n0 = splat16(-m);
       }
       const int k0 = (2 * x) % KS, k1 = (2 * x + 1) % KS;
       if (!second) {
