@@ -284,7 +284,7 @@ struct SegPlan {
 };
 
 struct QueryPlan {
-  int32_t rows = 0, row_waves = 4, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  int32_t rows = 0, row_waves = 4, key_ways = 1, row_groups = 0, n_split = 1, tiles_per_split = 1;
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
@@ -296,6 +296,9 @@ void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max
   // spread evenly over the fewest row groups.
   qp.row_groups = (int32_t)cdiv(qp.rows, 128);
   qp.row_waves = (int32_t)cdiv(cdiv(qp.rows, qp.row_groups), 32);
+  // Up to 64 rows: two wavefronts per 32 rows, each on one half of every key
+  // tile, so that the matrix cores of all four SIMDs take part.
+  qp.key_ways = qp.rows <= 64 ? 2 : 1;
   const int64_t n_tiles = std::max<int64_t>(1, cdiv(max_ctx, kKeyTile));
   qp.n_split = 1;
   qp.tiles_per_split = (int32_t)n_tiles;
@@ -399,6 +402,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.batch = batch;
   qa.rows = qp.rows;
   qa.row_waves = qp.row_waves;
+  qa.key_ways = qp.key_ways;
   qa.row_groups = qp.row_groups;
   qa.n_split = qp.n_split;
   qa.tiles_per_split = qp.tiles_per_split;

@@ -130,6 +130,7 @@ struct QueryArgs {
   int32_t n_new, hq, hkv, batch;
   int32_t rows;           // n_new * (hq / hkv) packed rows per kv head
   int32_t row_waves;      // 32-row attention wavefronts per workgroup: 1 .. 4
+  int32_t key_ways;       // 2: two wavefronts per 32 rows, one per key half (row_waves <= 2)
   int32_t row_groups;     // row groups of 32 * row_waves rows
   int32_t n_split;        // key splits per (batch, kv head, row group)
   int32_t tiles_per_split;

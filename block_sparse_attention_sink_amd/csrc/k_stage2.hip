@@ -11,13 +11,15 @@
 //   k_new_kv_f32                   rotate the new tokens' K at their positions
 //                                  and append K/V to the row's context buffer
 //                                  (float32 path; bf16 does it in k_query_bf16).
-//   k_query_bf16<D, NWA>           split-K flash attention of the packed
+//   k_query_bf16<D, RW, KW>        split-K flash attention of the packed
 //                                  (token, head-in-group) rows of one KV head
 //                                  over a segment list, 32 rows per attention
 //                                  wavefront on the software-pipelined prefill
-//                                  core (pool blocks and new tokens are rotated
-//                                  while staged; new tokens are also appended
-//                                  to the context buffer).
+//                                  core, RW row wavefronts, each doubled into
+//                                  two key halves when KW = 2 (pool blocks and
+//                                  new tokens are rotated while staged; new
+//                                  tokens are also appended to the context
+//                                  buffer).
 //   k_combine                      log-sum-exp merge of the split partials.
 //   k_query_f32                    float32 rows (one wavefront per row).
 #include "dbsa_device.hpp"
@@ -139,13 +141,181 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
+// The flash core on one half of every 64-key tile (keys 32h .. 32h + 31):
+// two wavefronts share a row set, each running this on its own half with its
+// own (m, l, O), merged once at the end.  Same lane layout, pipeline split
+// (pv_head / exp_next) and lazy reference as the full-tile core; half the
+// MFMAs and exponentials per wavefront and tile.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FlashHalf {
+  static constexpr int KS = D / 16;
+  static constexpr int OT = D / 32;
+  static constexpr int NPV = 2 * OT;  // P V products per half tile (2 k-steps of 16 keys x OT)
+  using Gm = TileGeom<D>;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  f32x16 o[OT];
+  float m, l;
+  bool have;
+  int h;  // key half (wave-uniform)
+
+  __device__ __forceinline__ void init(int half) {
+#pragma unroll
+    for (int t = 0; t < OT; ++t) o[t] = f32x16{};
+    m = 0.0f;
+    l = 0.0f;
+    have = false;
+    h = half;
+  }
+  // V^T fragment of P V product j of this half: k-step 2h + j / OT.
+  __device__ __forceinline__ bf16x8 vfrag(const char* st_v, const int (&vbase)[OT], int j) const {
+    const char* a0 = st_v + vbase[j % OT] + (16 * (2 * h + j / OT)) * Gm::ROW;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(a0 + 8 * Gm::ROW));
+    const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v8);
+  }
+  __device__ __forceinline__ bf16x8 kfrag(const char* st_k, const int (&koff)[KS], int ks) const {
+    return *reinterpret_cast<const bf16x8*>(st_k + koff[ks] + h * 32 * Gm::KROW);
+  }
+  __device__ __forceinline__ void scores(const char* st_k, const int (&koff)[KS],
+                                         const bf16x8 (&qb)[KS], f32x16& s) const {
+    s = splat16(-m);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(st_k, koff, ks), qb[ks], s, 0, 0, 0);
+  }
+  __device__ __forceinline__ void pv(const char* st_v, const int (&vbase)[OT], const bf16x8 (&p)[2]) {
+#pragma unroll
+    for (int j = 0; j < NPV; ++j)
+      o[j % OT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(st_v, vbase, j), p[j / OT],
+                                                          o[j % OT], 0, 0, 0);
+  }
+  // Mask, row maximum (16 scores a lane), rare reference raise; the previous
+  // half tile's P V interleaved with the maximum tree.
+  template <bool PV, typename Vis>
+  __device__ __forceinline__ void pv_head(const char* st_v, const int (&vbase)[OT],
+                                          const bf16x8 (&p)[2], f32x16& s, bool mask, Vis vis) {
+    if (mask) {
+      keep_branch();
+      const int hh = (threadIdx.x >> 5) & 1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = 32 * h + (i >> 2) * 8 + hh * 4 + (i & 3);
+        s[i] = vis(kr) ? s[i] : kNegInf;
+      }
+    }
+    float mq[8];
+    auto max_step = [&](int j) {
+      if (j < 8) {
+        mq[j] = __builtin_fmaxf(s[2 * j], s[2 * j + 1]);
+      } else if (j < 12) {
+        mq[j - 8] = __builtin_fmaxf(mq[j - 8], mq[j - 4]);
+      } else if (j < 14) {
+        mq[j - 12] = __builtin_fmaxf(mq[j - 12], mq[j - 10]);
+      } else if (j == 14) {
+        mq[0] = __builtin_fmaxf(mq[0], mq[1]);
+      }
+    };
+    if constexpr (PV) {
+      bf16x8 va[3];
+      va[0] = vfrag(st_v, vbase, 0);
+      va[1] = vfrag(st_v, vbase, 1);
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        if (j + 2 < NPV) va[(j + 2) % 3] = vfrag(st_v, vbase, j + 2);
+        o[j % OT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j % 3], p[j / OT], o[j % OT], 0, 0, 0);
+        max_step(2 * j);
+        max_step(2 * j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 2 * NPV; j < 15; ++j) max_step(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 15; ++j) max_step(j);
+    }
+    const float mx = max_xor32(mq[0]);
+    const bool need = mx > kLazy || (!have && mx > kNegInf);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      keep_branch();
+      const float delta = need ? mx : 0.0f;
+      const float alpha = have ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
+      m += delta;
+      have = have || mx > kNegInf;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] -= delta;
+#pragma unroll
+      for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+  }
+  // P = 2^s packed to bf16 into p, row sum into l; the next half tile's
+  // scores (relative to m) into n, in KS / 2 fenced groups of two MFMAs.
+  __device__ __forceinline__ void exp_next(const char* st_k, const int (&koff)[KS],
+                                           const bf16x8 (&qb)[KS], f32x16& s, bf16x8 (&p)[2],
+                                           f32x16& n) {
+    static_assert(KS == 8 || KS == 4, "head dim 128 or 64");
+    constexpr int NG = KS / 2;
+    constexpr int PPG = 8 / NG;  // score pairs per group
+    uint32_t w[8];
+    float sq[8];
+    auto fin = [&](int u) {
+      w[u] = pack_bf16x2(s[2 * u], s[2 * u + 1]);
+      sq[u] = s[2 * u] + s[2 * u + 1];
+    };
+    bf16x8 ka[2][2];
+    auto kread = [&](int x, int b) {
+      ka[b][0] = kfrag(st_k, koff, 2 * x);
+      ka[b][1] = kfrag(st_k, koff, 2 * x + 1);
+    };
+    n = splat16(-m);
+    kread(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < NG; ++x) {
+      if (x + 1 < NG) kread(x + 1, (x + 1) & 1);
+      n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][0], qb[2 * x], n, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < PPG; ++e) {
+        const int pr = x * PPG + e;
+        s[2 * pr] = __builtin_amdgcn_exp2f(s[2 * pr]);
+        s[2 * pr + 1] = __builtin_amdgcn_exp2f(s[2 * pr + 1]);
+      }
+      n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x & 1][1], qb[2 * x + 1], n, 0, 0, 0);
+      if (x > 0)
+#pragma unroll
+        for (int e = 0; e < PPG; ++e) fin((x - 1) * PPG + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < PPG; ++e) fin((NG - 1) * PPG + e);
+#pragma unroll
+    for (int w2 = 4; w2 > 0; w2 >>= 1)
+#pragma unroll
+      for (int k = 0; k < w2; ++k) sq[k] += sq[k + w2];
+    l += sq[0];
+    p[0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    p[1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
+  }
+  __device__ __forceinline__ float total() const { return sum_xor32(l); }
+};
+
+// ---------------------------------------------------------------------------
 // Query attention, bf16 MFMA, split-K over the context.
 //
 // Rows = (query token, head in GQA group) packed per KV head.  Workgroup =
-// NWA attention wavefronts of 32 packed rows each (the software-
-// pipelined Flash core of the prefill, on v_mfma_f32_32x32x16_bf16) plus
+// RW attention wavefronts of 32 packed rows each (the software-pipelined
+// Flash core of the prefill, on v_mfma_f32_32x32x16_bf16) plus
 // kQueryLoaders loader wavefronts, one of each kind per SIMD: a 32-row
-// attention wavefront needs half of a SIMD's registers.  Iteration i of the
+// attention wavefront needs half of a SIMD's registers.  With KW = 2 (at
+// most 64 rows) every row wavefront has a twin on the other half of each
+// key tile, so all four SIMDs run attention; the twins merge their (m, l, O)
+// through LDS after the last tile.  Iteration i of the
 // attention computes the softmax of tile i, P V of tile i - 1 and the scores
 // of tile i + 1, so it reads K of tile i + 1 and V of tile i - 1; meanwhile
 // the loaders store K and V of tile i + 2 (K ring of two LDS stages, V ring
@@ -157,9 +327,11 @@ __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
 // angles in registers, the tile's angles from a small table).  New tokens
 // (their rotated K and their V) also go to the context buffer.
 // ---------------------------------------------------------------------------
-template <int D, int NWA>
-__global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(QueryArgs a) {
+template <int D, int RW, int KW>
+__global__ __launch_bounds__(64 * (RW * KW + kQueryLoaders), 1) void k_query_bf16(QueryArgs a) {
   using Gm = TileGeom<D>;
+  static_assert(KW == 1 || (KW == 2 && RW <= 2), "key halves for at most 64 rows");
+  constexpr int NWA = RW * KW;  // attention wavefronts
   constexpr int NL = kQueryLoaders, NW = NWA + NL;
   constexpr int KS = D / 16, OT = D / 32, CP = D / 16, CR = D / 8, H = D / 2;
   constexpr int P = kQueryLead;
@@ -188,7 +360,8 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
   if (w >= W) return;  // padding of the last group of 8 (before any barrier)
   const int g = w % a.hkv, split = (w / a.hkv) % a.n_split, b = w / (a.hkv * a.n_split);
   const int G = a.hq / a.hkv;
-  const int rho = rg * (32 * NWA) + wave * 32 + col;
+  const int way = wave / RW;  // key half (KW == 2) of an attention wavefront
+  const int rho = rg * (32 * RW) + (wave % RW) * 32 + col;
   const bool live = !loader && rho < a.rows;
   const int r = live ? rho / G : 0;
   const int head = g * G + (live ? rho - (rho / G) * G : 0);
@@ -221,6 +394,7 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     const int ltid = tid - 64 * NWA;
     if (cnt == 0) {
       barrier_nofence();
+      if constexpr (KW == 2) barrier_nofence();  // (the key halves' merge)
       return;
     }
     // Item k of this thread: row ltid / CP + k * 64 / ITEMS, chunks c and
@@ -378,6 +552,7 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     static_for<P>([&](auto t) __attribute__((always_inline)) {
       if (l0 + (int)decltype(t)::value < cnt) step(t, l0 + (int)decltype(t)::value);
     });
+    if constexpr (KW == 2) barrier_nofence();  // (the key halves' merge)
     return;
   }
 
@@ -395,8 +570,6 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
-  Flash<D> fl;
-  fl.init();
   int koff[KS], vbase[OT];
   lane_offsets<D>(lane, koff, vbase);
   const auto kst = [&](int i) { return kring + (i & 1) * Gm::KBYTES; };
@@ -408,9 +581,12 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     const int lim = qpos - (it0 + i) * kKeyTile;
     return [=](int kr) { return kr <= lim; };
   };
+  std::conditional_t<KW == 1, Flash<D>, FlashHalf<D>> fl;
+  if constexpr (KW == 1) fl.init();
+  else fl.init(way);
   if (cnt == 0) {
     barrier_nofence();
-  } else {
+  } else if constexpr (KW == 1) {
     barrier_nofence();  // (the loaders' tile angles)
     barrier_nofence();  // tiles 0 and 1 stored
     f32x16 s0, s1, n0, n1;
@@ -435,6 +611,63 @@ __global__ __launch_bounds__(64 * (NWA + kQueryLoaders), 1) void k_query_bf16(Qu
     waitcnt<0, 0>();
     barrier_nofence();
     fl.pv(vst(cnt - 1), vbase, pr);
+  } else {
+    // The same schedule on this wavefront's half of every tile.
+    barrier_nofence();
+    barrier_nofence();
+    f32x16 s, n;
+    bf16x8 pr[2];
+    fl.scores(kst(0), koff, qb, s);
+    waitcnt<0, 0>();
+    barrier_nofence();
+    fl.template pv_head<false>(vst(0), vbase, pr, s, mask_of(0), vis_of(0));
+    fl.exp_next(kst(1), koff, qb, s, pr, n);
+    for (int i = 1; i < cnt; i += 2) {
+      waitcnt<0, 0>();
+      barrier_nofence();
+      fl.template pv_head<true>(vst(i - 1), vbase, pr, n, mask_of(i), vis_of(i));
+      fl.exp_next(kst(i + 1), koff, qb, n, pr, s);
+      if (i + 1 >= cnt) break;
+      waitcnt<0, 0>();
+      barrier_nofence();
+      fl.template pv_head<true>(vst(i), vbase, pr, s, mask_of(i + 1), vis_of(i + 1));
+      fl.exp_next(kst(i + 2), koff, qb, s, pr, n);
+    }
+    waitcnt<0, 0>();
+    barrier_nofence();
+    fl.pv(vst(cnt - 1), vbase, pr);
+  }
+  if constexpr (KW == 2) {
+    // Merge the second key half into the first, lane by lane (the same row
+    // and head dims), through the K ring and the angle table: both are idle
+    // once the last barrier has passed.
+    float* xo = reinterpret_cast<float*>(kring) + (wave % RW) * (16 * OT * 64) + lane;
+    float* xm = reinterpret_cast<float*>(&rot_a[0][0]) + (wave % RW) * (3 * 64) + lane;
+    static_assert(RW * 16 * OT * 64 * 4 <= 2 * Gm::KBYTES && RW * 3 * 64 * 4 <= sizeof(rot_a),
+                  "merge buffers fit the idle LDS");
+    if (way == 1) {
+#pragma unroll
+      for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xo[(t * 16 + i) * 64] = fl.o[t][i];
+      xm[0] = fl.m;
+      xm[64] = fl.l;
+      xm[128] = fl.have ? 1.0f : 0.0f;
+    }
+    __syncthreads();
+    if (way == 1) return;
+    const bool h0 = fl.have, h1 = xm[128] != 0.0f;
+    const float m1 = xm[64 * 0], l1 = xm[64];
+    const float mm = h0 && h1 ? __builtin_fmaxf(fl.m, m1) : (h0 ? fl.m : m1);
+    const float a0 = h0 ? __builtin_amdgcn_exp2f(fl.m - mm) : 0.0f;
+    const float a1 = h1 ? __builtin_amdgcn_exp2f(m1 - mm) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < OT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) fl.o[t][i] = fl.o[t][i] * a0 + xo[(t * 16 + i) * 64] * a1;
+    fl.m = mm;
+    fl.l = fl.l * a0 + l1 * a1;
+    fl.have = h0 || h1;
   }
   const float lsum = fl.total();
   if (!live) return;
@@ -645,11 +878,17 @@ template <int D>
 static void launch_query_d(const QueryArgs& a, dim3 grid, hipStream_t stream) {
   const int w = a.n_split * a.hkv * grid.z;
   grid = dim3(a.row_groups > 1 ? (w + 7) / 8 * 8 * a.row_groups : w);
+  constexpr int L = 64 * kQueryLoaders;
+  if (a.key_ways == 2) {
+    if (a.row_waves == 1) hipLaunchKernelGGL((k_query_bf16<D, 1, 2>), grid, dim3(L + 128), 0, stream, a);
+    else hipLaunchKernelGGL((k_query_bf16<D, 2, 2>), grid, dim3(L + 256), 0, stream, a);
+    return;
+  }
   switch (a.row_waves) {
-    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1>), grid, dim3(64 * (1 + kQueryLoaders)), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2>), grid, dim3(64 * (2 + kQueryLoaders)), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((k_query_bf16<D, 3>), grid, dim3(64 * (3 + kQueryLoaders)), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_query_bf16<D, 4>), grid, dim3(64 * (4 + kQueryLoaders)), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_query_bf16<D, 1, 1>), grid, dim3(L + 64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_query_bf16<D, 2, 1>), grid, dim3(L + 128), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_query_bf16<D, 3, 1>), grid, dim3(L + 192), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_query_bf16<D, 4, 1>), grid, dim3(L + 256), 0, stream, a); break;
   }
 }
 
@@ -661,7 +900,9 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
     else hipLaunchKernelGGL(k_query_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  if (a.row_waves < 1 || a.row_waves > 4) return hipErrorInvalidValue;
+  if (a.row_waves < 1 || a.row_waves > 4 || a.key_ways < 1 || a.key_ways > 2 ||
+      (a.key_ways == 2 && (a.row_waves > 2 || a.row_groups != 1)))
+    return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
   if (head_dim == 128) launch_query_d<128>(a, grid, stream);
   else launch_query_d<64>(a, grid, stream);
