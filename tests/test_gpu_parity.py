@@ -282,6 +282,25 @@ def test_query_many_rows_head_dim_64_and_three_waves():
                  195, True)
 
 
+def test_query_key_halves_row_counts():
+    """At most 64 packed rows per KV head run two wavefronts per row set, one
+    per half of every key tile, merged at the end: 1, 32, 33 and 40 rows (a
+    second row wavefront partly live), both head dims, with split-K over a
+    long context and without it over a short one."""
+    rng = np.random.default_rng(53)
+    short = rng.integers(30, 60, size=6).astype(np.int32)
+    long_lens = rng.integers(400, 1200, size=10).astype(np.int32)
+    ids_s = np.array([[0, 2, 5]], np.int32)
+    ids_l = np.array([[0, 3, 4, 8], [0, 1, 6, 9]], np.int32)
+    for fused in (False, True):
+        for d in (64, 128):
+            _stage2_case("bf16", 8, 2, d, short, ids_s, 10, 1e4, 211 + d, fused)      # 40 rows, one split
+            _stage2_case("bf16", 8, 2, d, long_lens, ids_l, 10, 5e5, 213 + d, fused)  # 40 rows, split-K
+        _stage2_case("bf16", 4, 4, 128, long_lens, ids_l, 1, 1e4, 217, fused)         # 1 row (MHA decode)
+        _stage2_case("bf16", 8, 2, 128, long_lens, ids_l[:1], 8, 1e4, 219, fused)     # 32 rows
+        _stage2_case("bf16", 2, 2, 64, short, ids_s, 33, 1e4, 221, fused)             # 33 rows
+
+
 def test_query_odd_head_count_pads_the_grid():
     """3 KV heads x 4-head groups x 48 tokens = 192 rows in two row groups: the
     (split, head) work items are not a multiple of 8, so the grid carries
