@@ -42,11 +42,11 @@ class AttnT(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("rope_inv_freq", ctypes.POINTER(ctypes.c_double))]
+                ("rope_inv_freq", ctypes.c_void_p)]  # const double*
 
 
 class BlocksT(ctypes.Structure):
-    _fields_ = [("block_lens", ctypes.POINTER(ctypes.c_int32)), ("n_blocks", ctypes.c_int32),
+    _fields_ = [("block_lens", ctypes.c_void_p), ("n_blocks", ctypes.c_int32),  # const int32_t*
                 ("sink", ctypes.c_int32), ("j", ctypes.c_int32)]
 
 
@@ -64,7 +64,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     pa, pb = ctypes.POINTER(AttnT), ctypes.POINTER(BlocksT)
-    p32, p64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    # Host arrays (const int32_t* / const int64_t*) go as plain addresses.
+    p32 = p64 = vp
     lib.dbsa_prefill.argtypes = [pa, pb, vp, vp, vp, vp, vp, sz, vp]
     lib.dbsa_prefill_layers.argtypes = [pa, pb, i32, vp, i64, vp, vp, i64, vp, i64, vp, sz, vp]
     lib.dbsa_append_block.argtypes = [pa, pb, i32, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
@@ -106,8 +107,7 @@ def attn_t(n_q_heads, n_kv_heads, head_dim, dtype, theta, scale=None) -> AttnT:
     if w.size != head_dim // 2:
         raise DbsaError(EINVAL, f"rope frequency table has {w.size} entries, "
                                 f"head_dim / 2 = {head_dim // 2} needed")
-    a = AttnT(n_q_heads, n_kv_heads, head_dim, dtype, 1.0e4, sc,
-              w.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    a = AttnT(n_q_heads, n_kv_heads, head_dim, dtype, 1.0e4, sc, _addr(w))
     a._keep = w  # the table must outlive the call
     return a
 
@@ -134,8 +134,7 @@ class Blocks:
 
     def __init__(self, block_lens, sink: int, j: int):
         self.lens = np.ascontiguousarray(np.asarray(block_lens, dtype=np.int32))
-        self.t = BlocksT(self.lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                         int(self.lens.size), int(sink), int(j))
+        self.t = BlocksT(_addr(self.lens), int(self.lens.size), int(sink), int(j))
 
 
 def _dtype_code(t) -> int:
@@ -159,8 +158,16 @@ def _ptr(t, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _addr(arr: np.ndarray) -> int:
+    """Address of a host array's data (the array must outlive the call)."""
+    return arr.__array_interface__["data"][0]
+
+
 def _stream(device) -> int:
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -168,10 +175,9 @@ _ws_cache = {}
 
 
 def _workspace(nbytes: int, device):
-    """Per-device workspace, grown on demand (calls on one stream are ordered)."""
+    """Per-device workspace (at least 1 MiB), grown on demand (calls on one
+    stream are ordered)."""
     import torch
-    if nbytes == 0:
-        return None
     key = str(device)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -180,12 +186,33 @@ def _workspace(nbytes: int, device):
     return ws
 
 
-def _ws_ptr(ws):
-    return 0 if ws is None else ws.data_ptr()
+def _run(device, call, need):
+    """call(ws_ptr, ws_bytes) with the device's cached workspace.  A call that
+    returns DBSA_ENOSPC has enqueued nothing: the workspace grows to need()
+    bytes and the call is made once more."""
+    ws = _ws_cache.get(str(device))
+    if ws is None:
+        ws = _workspace(0, device)
+    rc = call(ws.data_ptr(), ws.numel())
+    if rc == ENOSPC:
+        ws = _workspace(need(), device)
+        rc = call(ws.data_ptr(), ws.numel())
+    _check(rc)
 
 
-def _ws_size(ws):
-    return 0 if ws is None else ws.numel()
+def _need(op, a, b, rows=0, batch=1, n_ids=0, max_ctx=0) -> int:
+    lib = load()
+    n = lib.dbsa_workspace_bytes(op, ctypes.byref(a), None if b is None else ctypes.byref(b.t),
+                                 int(rows), int(batch), int(n_ids), int(max_ctx))
+    if n == 0 and lib.dbsa_last_error():
+        _check(EINVAL)
+    return int(n)
+
+
+def _max_selected(block_lens, ids: np.ndarray) -> int:
+    """Largest total length of one row's selected blocks."""
+    lens = np.asarray(block_lens, dtype=np.int64)
+    return int(lens[np.clip(ids, 0, lens.size - 1)].sum(axis=1).max())
 
 
 def dbsa_workspace_bytes(op, n_q_heads, n_kv_heads, head_dim, dtype, theta=1e4, block_lens=None,
@@ -213,13 +240,10 @@ def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=
     b = Blocks(block_lens, sink, j)
     if out is None:
         out = torch.empty_like(q)
-    need = lib.dbsa_workspace_bytes(OP_PREFILL, ctypes.byref(a), ctypes.byref(b.t), 0, 1, 0, 0)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q.device)
-    _check(lib.dbsa_prefill(ctypes.byref(a), ctypes.byref(b.t), _ptr(q, "q"),
-                            _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), _ptr(out, "out", q.dtype),
-                            _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    args = (ctypes.byref(a), ctypes.byref(b.t), _ptr(q, "q"), _ptr(k, "k", q.dtype),
+            _ptr(v, "v", q.dtype), _ptr(out, "out", q.dtype))
+    st = _stream(q.device)
+    _run(q.device, lambda wp, wn: lib.dbsa_prefill(*args, wp, wn, st), lambda: _need(OP_PREFILL, a, b))
     return out
 
 
@@ -246,14 +270,12 @@ def dbsa_prefill_layers(q, k, v, block_lens, sink: int, j: int, theta, scale=Non
     if out is None:
         out = torch.empty((n_layers, n, hq, d), dtype=q.dtype, device=q.device)
     stride = lambda t: 0 if t.shape[0] == 1 else t[0].numel()
-    need = lib.dbsa_workspace_bytes(OP_PREFILL, ctypes.byref(a), ctypes.byref(b.t), 0, 1, 0, 0)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q.device)
-    _check(lib.dbsa_prefill_layers(
-        ctypes.byref(a), ctypes.byref(b.t), n_layers, _ptr(ql, "q"), stride(ql),
-        _ptr(kl, "k", q.dtype), _ptr(vl, "v", q.dtype), stride(kl), _ptr(out, "out", q.dtype),
-        out[0].numel(), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    args = (ctypes.byref(a), ctypes.byref(b.t), n_layers, _ptr(ql, "q"), stride(ql),
+            _ptr(kl, "k", q.dtype), _ptr(vl, "v", q.dtype), stride(kl), _ptr(out, "out", q.dtype),
+            out[0].numel())
+    st = _stream(q.device)
+    _run(q.device, lambda wp, wn: lib.dbsa_prefill_layers(*args, wp, wn, st),
+         lambda: _need(OP_PREFILL, a, b))
     return out
 
 
@@ -269,18 +291,13 @@ def dbsa_append_block(q_new, k_new, v_new, k_cache, v_cache, block_lens, sink: i
     b = Blocks(block_lens, sink, j)
     if out is None:
         out = torch.empty_like(q_new)
-    need = lib.dbsa_workspace_bytes(OP_APPEND, ctypes.byref(a), ctypes.byref(b.t), new_len, 1, 0,
-                                    0)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q_new.device)
-    _check(lib.dbsa_append_block(ctypes.byref(a), ctypes.byref(b.t), int(new_len),
-                                 _ptr(q_new, "q_new"), _ptr(k_new, "k_new", q_new.dtype),
-                                 _ptr(v_new, "v_new", q_new.dtype),
-                                 _ptr(k_cache, "k_cache", q_new.dtype),
-                                 _ptr(v_cache, "v_cache", q_new.dtype), int(k_cache.shape[0]),
-                                 _ptr(out, "out", q_new.dtype), _ws_ptr(ws), _ws_size(ws),
-                                 _stream(q_new.device)))
+    args = (ctypes.byref(a), ctypes.byref(b.t), int(new_len), _ptr(q_new, "q_new"),
+            _ptr(k_new, "k_new", q_new.dtype), _ptr(v_new, "v_new", q_new.dtype),
+            _ptr(k_cache, "k_cache", q_new.dtype), _ptr(v_cache, "v_cache", q_new.dtype),
+            int(k_cache.shape[0]), _ptr(out, "out", q_new.dtype))
+    st = _stream(q_new.device)
+    _run(q_new.device, lambda wp, wn: lib.dbsa_append_block(*args, wp, wn, st),
+         lambda: _need(OP_APPEND, a, b, rows=new_len))
     return out
 
 
@@ -300,24 +317,17 @@ def dbsa_gather_rope(k_pool, v_pool, block_lens, ids, theta: float, n_q_heads: O
     ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
     batch, n_ids = ids.shape
     if capacity is None:
-        lens = np.asarray(block_lens, dtype=np.int64)
-        capacity = int(max(lens[np.clip(r, 0, lens.size - 1)].sum() for r in ids))
+        capacity = _max_selected(block_lens, ids)
     if k_out is None:
         k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
         v_out = torch.empty_like(k_out)
     ctx = np.zeros(batch, dtype=np.int64)
-    need = lib.dbsa_workspace_bytes(OP_GATHER, ctypes.byref(a), ctypes.byref(b.t), 0, batch, n_ids,
-                                    0)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, k_pool.device)
-    _check(lib.dbsa_gather_rope(ctypes.byref(a), ctypes.byref(b.t),
-                                ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_ids, batch,
-                                _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
-                                _ptr(k_out, "k_out", k_pool.dtype),
-                                _ptr(v_out, "v_out", k_pool.dtype), int(k_out.shape[1]),
-                                ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ws_ptr(ws),
-                                _ws_size(ws), _stream(k_pool.device)))
+    args = (ctypes.byref(a), ctypes.byref(b.t), _addr(ids), n_ids, batch, _ptr(k_pool, "k_pool"),
+            _ptr(v_pool, "v_pool", k_pool.dtype), _ptr(k_out, "k_out", k_pool.dtype),
+            _ptr(v_out, "v_out", k_pool.dtype), int(k_out.shape[1]), _addr(ctx))
+    st = _stream(k_pool.device)
+    _run(k_pool.device, lambda wp, wn: lib.dbsa_gather_rope(*args, wp, wn, st),
+         lambda: _need(OP_GATHER, a, b, batch=batch, n_ids=n_ids))
     return k_out, v_out, ctx
 
 
@@ -337,18 +347,14 @@ def dbsa_query_attn(q, k_new, v_new, k_ctx, v_ctx, ctx_len: Sequence[int], theta
         out = torch.empty_like(q)
     if n_new == 0:
         return out
-    b = Blocks([1], 1, 0)
-    need = lib.dbsa_workspace_bytes(OP_QUERY, ctypes.byref(a), ctypes.byref(b.t), n_new, batch, 0,
-                                    int(ctx.max()) + n_new)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q.device)
-    _check(lib.dbsa_query_attn(ctypes.byref(a), batch, n_new, _ptr(q, "q"),
-                               _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
-                               _ptr(k_ctx, "k_ctx", q.dtype), _ptr(v_ctx, "v_ctx", q.dtype),
-                               ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                               int(k_ctx.shape[1]), _ptr(out, "out", q.dtype), _ws_ptr(ws),
-                               _ws_size(ws), _stream(q.device)))
+    args = (ctypes.byref(a), batch, n_new, _ptr(q, "q"), _ptr(k_new, "k_new", q.dtype),
+            _ptr(v_new, "v_new", q.dtype), _ptr(k_ctx, "k_ctx", q.dtype),
+            _ptr(v_ctx, "v_ctx", q.dtype), _addr(ctx), int(k_ctx.shape[1]),
+            _ptr(out, "out", q.dtype))
+    st = _stream(q.device)
+    _run(q.device, lambda wp, wn: lib.dbsa_query_attn(*args, wp, wn, st),
+         lambda: _need(OP_QUERY, a, Blocks([1], 1, 0), rows=n_new, batch=batch,
+                       max_ctx=int(ctx.max()) + n_new))
     return out
 
 
@@ -372,20 +378,15 @@ def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k
         out = torch.empty_like(q)
     if n_new == 0:
         return out
-    lens = np.asarray(block_lens, dtype=np.int64)
-    tp = max(int(lens[np.clip(r, 0, lens.size - 1)].sum()) for r in ids)
-    need = lib.dbsa_workspace_bytes(OP_QUERY_GATHERED, ctypes.byref(a), ctypes.byref(b.t), n_new,
-                                    batch, n_ids, tp + int(tl.max()) + n_new)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q.device)
-    _check(lib.dbsa_query_attn_gathered(
-        ctypes.byref(a), ctypes.byref(b.t), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        n_ids, batch, _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new,
-        _ptr(q, "q"), _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
-        _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype),
-        tl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(k_tail.shape[1]),
-        _ptr(out, "out", q.dtype), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    args = (ctypes.byref(a), ctypes.byref(b.t), _addr(ids), n_ids, batch,
+            _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new, _ptr(q, "q"),
+            _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+            _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype), _addr(tl),
+            int(k_tail.shape[1]), _ptr(out, "out", q.dtype))
+    st = _stream(q.device)
+    _run(q.device, lambda wp, wn: lib.dbsa_query_attn_gathered(*args, wp, wn, st),
+         lambda: _need(OP_QUERY_GATHERED, a, b, rows=n_new, batch=batch, n_ids=n_ids,
+                       max_ctx=_max_selected(block_lens, ids) + int(tl.max()) + n_new))
     return out
 
 
@@ -416,17 +417,13 @@ def dbsa_gather_rope_spans(k_pool, v_pool, span_src, span_len, theta,
         k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
         v_out = torch.empty_like(k_out)
     ctx = np.zeros(batch, dtype=np.int64)
-    need = lib.dbsa_workspace_bytes(OP_GATHER_SPANS, ctypes.byref(a), None, 0, batch, n_spans, 0)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, k_pool.device)
-    _check(lib.dbsa_gather_rope_spans(
-        ctypes.byref(a), src.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_spans, batch, int(n_pool),
-        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
-        _ptr(k_out, "k_out", k_pool.dtype), _ptr(v_out, "v_out", k_pool.dtype),
-        int(k_out.shape[1]), ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ws_ptr(ws),
-        _ws_size(ws), _stream(k_pool.device)))
+    args = (ctypes.byref(a), _addr(src), _addr(ln), n_spans, batch, int(n_pool),
+            _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+            _ptr(k_out, "k_out", k_pool.dtype), _ptr(v_out, "v_out", k_pool.dtype),
+            int(k_out.shape[1]), _addr(ctx))
+    st = _stream(k_pool.device)
+    _run(k_pool.device, lambda wp, wn: lib.dbsa_gather_rope_spans(*args, wp, wn, st),
+         lambda: _need(OP_GATHER_SPANS, a, None, batch=batch, n_ids=n_spans))
     return k_out, v_out, ctx
 
 
@@ -448,18 +445,13 @@ def dbsa_query_attn_spans(q, k_new, v_new, k_pool, v_pool, span_src, span_len, k
         out = torch.empty_like(q)
     if n_new == 0:
         return out
-    tp = int(ln.clip(min=0).sum(axis=1).max())
-    need = lib.dbsa_workspace_bytes(OP_QUERY_SPANS, ctypes.byref(a), None, n_new, batch, n_spans,
-                                    tp + int(tl.max()) + n_new)
-    if need == 0 and lib.dbsa_last_error():
-        _check(EINVAL)
-    ws = _workspace(need, q.device)
-    _check(lib.dbsa_query_attn_spans(
-        ctypes.byref(a), src.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_spans, batch, int(k_pool.shape[0]),
-        _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new, _ptr(q, "q"),
-        _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
-        _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype),
-        tl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(k_tail.shape[1]),
-        _ptr(out, "out", q.dtype), _ws_ptr(ws), _ws_size(ws), _stream(q.device)))
+    args = (ctypes.byref(a), _addr(src), _addr(ln), n_spans, batch, int(k_pool.shape[0]),
+            _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new, _ptr(q, "q"),
+            _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+            _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype), _addr(tl),
+            int(k_tail.shape[1]), _ptr(out, "out", q.dtype))
+    st = _stream(q.device)
+    _run(q.device, lambda wp, wn: lib.dbsa_query_attn_spans(*args, wp, wn, st),
+         lambda: _need(OP_QUERY_SPANS, a, None, rows=n_new, batch=batch, n_ids=n_spans,
+                       max_ctx=int(ln.clip(min=0).sum(axis=1).max()) + int(tl.max()) + n_new))
     return out
