@@ -129,6 +129,16 @@ def test_prefill_single_block_and_tiny_pool():
         assert_close(got, want, "bf16", f"prefill lens={lens.tolist()}")
 
 
+def test_prefill_one_token_blocks_every_pattern():
+    """Blocks of one to three tokens (many blocks per key tile, so every tile
+    is partial) under each sink / window pattern."""
+    rng = np.random.default_rng(61)
+    lens = rng.integers(1, 4, size=150).astype(np.int32)
+    for sink, j in PATTERNS:
+        got, want = _run_prefill(lens, 4, 2, 64, "bf16", sink, j, 1e4, seed=63)
+        assert_close(got, want, "bf16", f"prefill tiny blocks sink={sink} j={j}")
+
+
 def test_prefill_repeatable_bitwise():
     rng = np.random.default_rng(77)
     lens = rng.integers(50, 400, size=10).astype(np.int32)
@@ -299,6 +309,18 @@ def test_query_key_halves_row_counts():
         _stage2_case("bf16", 4, 4, 128, long_lens, ids_l, 1, 1e4, 217, fused)         # 1 row (MHA decode)
         _stage2_case("bf16", 8, 2, 128, long_lens, ids_l[:1], 8, 1e4, 219, fused)     # 32 rows
         _stage2_case("bf16", 2, 2, 64, short, ids_s, 33, 1e4, 221, fused)             # 33 rows
+
+
+def test_query_ten_row_groups():
+    """300 query tokens x 4-head groups = 1200 packed rows: ten row groups of
+    120 rows (four wavefronts), placed eight workgroup ids apart, with and
+    without split-K."""
+    rng = np.random.default_rng(59)
+    lens = rng.integers(100, 700, size=8).astype(np.int32)
+    for fused in (False, True):
+        _stage2_case("bf16", 8, 2, 128, lens, np.array([[0, 3, 6]], np.int32), 300, 1e4, 231, fused)
+    _stage2_case("bf16", 4, 1, 64, lens, np.array([[0, 1, 2, 4, 5, 7]], np.int32), 300, 5e5, 233,
+                 True)
 
 
 def test_query_odd_head_count_pads_the_grid():
