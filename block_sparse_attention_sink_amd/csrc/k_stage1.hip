@@ -229,19 +229,33 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   barrier_nofence();
   fl.pv(vst(n_tiles - 1), vbase, pr);
 
+  // O = O / l in bf16, staged row by row in the wave's part of the K ring
+  // (idle once the last barrier has passed: every K read and K load of the
+  // walk is done) so that whole 16-byte chunks of a row go out together;
+  // chunks are XOR-swizzled by row against LDS bank conflicts.
   const float lsum = fl.total();
-  if (t < r1) {
-    const float inv = 1.0f / lsum;
-    uint16_t* op = static_cast<uint16_t*>(a.o) + ((int64_t)(t - a.q_row0) * a.hq + head) * D;
+  const float inv = t < r1 ? 1.0f / lsum : 0.0f;
+  constexpr int CPR = D / 8;  // 16-byte chunks per output row
+  char* const ost = kring + wave * (kRowsPerWave * Gm::ROW);
+  static_assert(kPrefillWaves * kRowsPerWave * Gm::ROW <= NS * Gm::KBYTES, "O fits the K ring");
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
+  for (int m = 0; m < D / 32; ++m)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = m * 32 + q4 * 8 + hh * 4;
-        const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
-                         pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
+                       pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
+      const int ch = (m * 4 + q4) ^ (col & (CPR - 1));  // head dims 8 (m * 4 + q4) .. + 7
+      *reinterpret_cast<u32x2*>(ost + col * Gm::ROW + ch * 16 + hh * 8) = w;
+    }
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+    const int rr = i * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ost + rr * Gm::ROW + (ch ^ (rr & (CPR - 1))) * 16);
+    const int trow = r0 + wave * kRowsPerWave + rr;
+    if (trow < r1)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) +
+                                ((int64_t)(trow - a.q_row0) * a.hq + head) * D + ch * 8) = v;
   }
 }
 
