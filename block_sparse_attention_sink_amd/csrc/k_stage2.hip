@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_gather_bf16(GatherArgs a) {
   u32x4* ko = reinterpret_cast<u32x4*>(a.k_out);
   u32x4* vo = reinterpret_cast<u32x4*>(a.v_out);
   constexpr int CR = D / 8;
-  for (int g = 0; g < a.hkv; ++g) {
+  auto head = [&](int g) __attribute__((always_inline)) {
     const int64_t src = (src_tok * a.hkv + g) * CR;
     const int64_t dst = (((int64_t)b * a.cap + u) * a.hkv + g) * CR;
     u32x4 k1 = kp[src + c], k2 = kp[src + c + CP];
@@ -72,6 +72,14 @@ __global__ __launch_bounds__(256) void k_gather_bf16(GatherArgs a) {
     ko[dst + c + CP] = k2;
     vo[dst + c] = v1;
     vo[dst + c + CP] = v2;
+  };
+  // Many KV heads: four heads' loads in flight per thread (measured 8%
+  // faster with 32 heads; with 8 heads the plain loop is faster).
+  if (a.hkv >= 16) {
+#pragma unroll 4
+    for (int g = 0; g < a.hkv; ++g) head(g);
+  } else {
+    for (int g = 0; g < a.hkv; ++g) head(g);
   }
 }
 
