@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdbsa.so")
-SOURCES = ["dbsa_host.hip", "k_stage1.hip", "k_stage2.hip"]
+SOURCES = ["dbsa_host.hip", "k_stage1.hip", "k_stage2.hip", "k_tables.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -560,6 +560,13 @@ __device__ __forceinline__ int xcd_logical(int lin, int total) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// int32 table carried in the kernel arguments at byte offset `off` of the
+// argument block: read in place through the kernarg segment pointer (indexing
+// the by-value argument would make the compiler copy it to private memory).
+__device__ __forceinline__ const int32_t* kernarg_ints(size_t off) {
+  return reinterpret_cast<const int32_t*>((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
+}
+
 // Largest b in [0, n) with tab[b] <= t (tab ascending, tab[0] <= t).
 __device__ __forceinline__ int upper_index(const int32_t* tab, int n, int t) {
   int lo = 0, hi = n;

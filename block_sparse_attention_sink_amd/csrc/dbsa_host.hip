@@ -1,5 +1,5 @@
 // Host side of the DBSA library: argument checks, planning, workspace layout,
-// per-call table staging and kernel launches behind the C ABI in dbsa.h.
+// per-call tables and kernel launches behind the C ABI in dbsa.h.
 //
 // Method: "Efficient Many-Shot In-Context Learning with Dynamic Block-Sparse
 // Attention" (paper-notes page, ACL 2025), cited as [Notes, section].
@@ -10,8 +10,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
-#include <mutex>
 #include <vector>
 
 #include "dbsa.h"
@@ -125,62 +123,21 @@ float q_scale_of(const dbsa_attn_t* a) {
 size_t elem_bytes(const dbsa_attn_t* a) { return a->dtype == DBSA_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
-// Pinned staging ring: per-call tables go host -> device by an async copy on
-// the caller's stream from a slot that is reused only after its copy is done.
+// Per-call tables that do not fit the kernel arguments: written into the
+// workspace by k_upload launches on the caller's stream (kInlineInts ints per
+// launch).  Nothing is staged in host memory and the host never waits.
 // ---------------------------------------------------------------------------
-constexpr int kSlots = 16;
-constexpr size_t kSlotBytes = size_t(1) << 20;
+constexpr size_t kMaxTableBytes = size_t(1) << 20;
 
-struct Ring {
-  std::mutex mu;
-  char* host = nullptr;
-  hipEvent_t ev[kSlots] = {};
-  bool pending[kSlots] = {};
-  int next = 0;
-};
-
-std::mutex g_rings_mu;
-std::map<int, Ring*> g_rings;
-
-int stage_bytes(const void* src, size_t n, void* dst, hipStream_t s) {
-  if (n == 0) return DBSA_OK;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  Ring* r;
-  {
-    std::lock_guard<std::mutex> g(g_rings_mu);
-    Ring*& slot = g_rings[dev];
-    if (!slot) {
-      Ring* nr = new Ring();
-      e = hipHostMalloc(reinterpret_cast<void**>(&nr->host), kSlots * kSlotBytes,
-                        hipHostMallocDefault);
-      if (e != hipSuccess) {
-        delete nr;
-        return hip_fail(e, "hipHostMalloc(staging ring)");
-      }
-      for (int i = 0; i < kSlots; ++i) {
-        e = hipEventCreateWithFlags(&nr->ev[i], hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-      }
-      slot = nr;
-    }
-    r = slot;
+int upload_ints(const int32_t* src, size_t n, void* dst, hipStream_t s) {
+  for (size_t i = 0; i < n; i += kInlineInts) {
+    UploadArgs ua;
+    ua.dst = static_cast<int32_t*>(dst) + i;
+    ua.n = (int32_t)std::min<size_t>(kInlineInts, n - i);
+    std::memcpy(ua.v, src + i, (size_t)ua.n * sizeof(int32_t));
+    const hipError_t e = launch_upload(ua, s);
+    if (e != hipSuccess) return hip_fail(e, "launch upload");
   }
-  std::lock_guard<std::mutex> g(r->mu);
-  const int k = r->next;
-  r->next = (k + 1) % kSlots;
-  if (r->pending[k]) {
-    e = hipEventSynchronize(r->ev[k]);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging slot)");
-  }
-  char* h = r->host + (size_t)k * kSlotBytes;
-  std::memcpy(h, src, n);
-  e = hipMemcpyAsync(dst, h, n, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
-  e = hipEventRecord(r->ev[k], s);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  r->pending[k] = true;
   return DBSA_OK;
 }
 
@@ -225,14 +182,19 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
 
 int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Plan& p,
                   const void* q, int32_t q_row0, const void* k, const void* v, void* o,
-                  void* ws, hipStream_t s, bool stage_table = true) {
+                  void* ws, hipStream_t s, bool upload_table = true) {
   char* w = static_cast<char*>(ws);
-  if (stage_table) {  // (layers after the first reuse the table already staged)
-    const int rc = stage_bytes(p.off.data(), p.meta_bytes, w + p.off_meta, s);
+  // Block offsets: in the kernel arguments when they fit, else uploaded once
+  // (layers after the first reuse the uploaded table).
+  const bool inl = p.off.size() <= (size_t)kInlineInts;
+  if (!inl && upload_table) {
+    const int rc = upload_ints(p.off.data(), p.off.size(), w + p.off_meta, s);
     if (rc) return rc;
   }
   const RopeFreq freq = make_freq(a);
   PrefillArgs pa;
+  pa.n_inline = inl ? (int32_t)p.off.size() : 0;
+  if (inl) std::memcpy(pa.inl, p.off.data(), p.off.size() * sizeof(int32_t));
   pa.q = q;
   pa.o = o;
   pa.offsets = reinterpret_cast<const int32_t*>(w + p.off_meta);
@@ -354,7 +316,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   const bool inl = bf16 && sp.tables.size() <= (size_t)kInlineInts;
   const int32_t* dt = reinterpret_cast<const int32_t*>(w + qp.off_meta);
   if (!inl) {
-    const int rc = stage_bytes(sp.tables.data(), qp.meta_bytes, w + qp.off_meta, s);
+    const int rc = upload_ints(sp.tables.data(), sp.tables.size(), w + qp.off_meta, s);
     if (rc) return rc;
   }
   const RopeFreq freq = make_freq(a);
@@ -447,9 +409,9 @@ int check_ptrs(std::initializer_list<const void*> ps, const char* names) {
 }
 
 int check_meta(size_t bytes) {
-  if (bytes > kSlotBytes)
+  if (bytes > kMaxTableBytes)
     return fail(DBSA_EUNSUPPORTED, "per-call tables of %zu bytes exceed the %zu-byte limit",
-                bytes, kSlotBytes);
+                bytes, kMaxTableBytes);
   return DBSA_OK;
 }
 
@@ -752,15 +714,21 @@ int gather_spans(const dbsa_attn_t* attn, const RowSpans& rs, int32_t batch, con
   if (rc) return rc;
   for (int r = 0; r < batch; ++r) ctx_len_out[r] = lens[r];
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = stage_bytes(tables.data(), mb, ws, s);
-  if (rc) return rc;
   GatherArgs ga;
+  const bool inl = tables.size() <= (size_t)kInlineInts;
+  if (inl) {
+    std::memcpy(ga.inl, tables.data(), tables.size() * sizeof(int32_t));
+  } else {
+    rc = upload_ints(tables.data(), tables.size(), ws, s);
+    if (rc) return rc;
+  }
+  ga.n_inline = inl ? (int32_t)tables.size() : 0;
+  ga.tab = static_cast<const int32_t*>(ws);
+  ga.batch = batch;
   ga.k_pool = k_pool;
   ga.v_pool = v_pool;
   ga.k_out = k_out;
   ga.v_out = v_out;
-  ga.start = static_cast<const int32_t*>(ws);
-  ga.src = ga.start + (size_t)batch * (n + 1);
   ga.n_ids = n;
   ga.hkv = attn->n_kv_heads;
   ga.cap = out_capacity_tokens;

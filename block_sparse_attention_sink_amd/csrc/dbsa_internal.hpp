@@ -45,12 +45,25 @@ struct PackArgs {
   RopeFreq freq;
 };
 
+// Small per-call int32 tables travel in the kernel arguments (kInlineInts
+// ints at most, read through the kernarg segment pointer so no private copy
+// is made); larger ones are written into the workspace by k_upload launches,
+// each carrying kInlineInts ints in its own arguments.  Either way the copy
+// is ordered on the caller's stream and needs no host staging memory.
+constexpr int kInlineInts = 512;
+
+struct UploadArgs {
+  int32_t* dst;
+  int32_t n;
+  int32_t v[kInlineInts];
+};
+
 struct PrefillArgs {
   const void* q;            // [n_tokens][hq][d] unrotated (rows of this call)
   const void* k_tiles;      // from PackArgs
   const void* v;            // [n_keys][hkv][d] values (natural layout, read directly)
   void* o;                  // [rows][hq][d]
-  const int32_t* offsets;   // device int32[n_blocks + 1], block start tokens
+  const int32_t* offsets;   // device int32[n_blocks + 1], block start tokens (n_inline == 0)
   int32_t n_blocks;
   int32_t sink;
   int32_t j;
@@ -62,6 +75,8 @@ struct PrefillArgs {
   int32_t sink_tiles, win_tile0, n_slots;  // key-tile slot map (see PackArgs)
   float q_scale;            // softmax scale * log2(e), folded into Q
   RopeFreq freq;
+  int32_t n_inline;         // > 0: the offsets are `inl` below
+  int32_t inl[kInlineInts];
 };
 
 // ---------------------------------------------------------------------------
@@ -77,7 +92,6 @@ struct PrefillArgs {
 // The tables are int32 arrays at these offsets of one table block, which
 // travels in the kernel arguments when it fits (kInlineInts) and otherwise in
 // the workspace.
-constexpr int kInlineInts = 512;
 struct SegTable {
   int32_t o_start;   // [batch][stride]  (start[nseg] = context length)
   int32_t o_src;     // [batch][stride]
@@ -93,12 +107,15 @@ struct GatherArgs {
   const void* v_pool;
   void* k_out;            // [batch][cap][hkv][d]
   void* v_out;
-  const int32_t* start;   // [batch][n_ids + 1] output start token of each id
-  const int32_t* src;     // [batch][n_ids] pool start token of each id
-  int32_t n_ids, hkv;
+  const int32_t* tab;     // device table (n_inline == 0): start | src, see below
+  int32_t n_ids, hkv, batch;
   int64_t cap;
   int32_t max_len;        // max T'_b
   RopeFreq freq;
+  int32_t n_inline;       // > 0: the table is `inl` below
+  int32_t inl[kInlineInts];
+  // table: start [batch][n_ids + 1] (output start token of each id, then T'_b),
+  //        src [batch][n_ids] (pool start token of each id)
 };
 
 struct NewKVArgs {
@@ -148,6 +165,7 @@ struct CombineArgs {
 };
 
 // Launchers (each returns the launch status; all enqueue on `stream`).
+hipError_t launch_upload(const UploadArgs& a, hipStream_t stream);
 hipError_t launch_pack(const PackArgs& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int batch, int head_dim, int dtype,

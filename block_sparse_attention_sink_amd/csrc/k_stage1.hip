@@ -81,12 +81,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   // Visible key intervals [Notes, Method > Stage 1, item 2]:
   // row t sees [lo(t), t] with lo(t) = start of block max(blk(t) - j, 0),
   // plus the anchor block [0, sink_end) when the sink is on.
-  const int32_t* off = a.offsets;
+  const int32_t* off = a.n_inline ? kernarg_ints(offsetof(PrefillArgs, inl)) : a.offsets;
   const int nb = a.n_blocks;
-  const int sink_end = a.sink ? off[1] : 0;
+  // (The table may sit in the kernel arguments or in device memory, so the
+  // compiler cannot tell that the workgroup-wide values below are uniform:
+  // say so, which keeps them, and the tile addresses built from them, in
+  // scalar registers.)
+  const int sink_end = __builtin_amdgcn_readfirstlane(a.sink ? off[1] : 0);
   const int lo_t = off[max(upper_index(off, nb, min(t, r1 - 1)) - a.j, 0)];
-  const int lo_first = off[max(upper_index(off, nb, r0) - a.j, 0)];
-  const int lo_last = off[max(upper_index(off, nb, r1 - 1) - a.j, 0)];
+  const int lo_first = __builtin_amdgcn_readfirstlane(off[max(upper_index(off, nb, r0) - a.j, 0)]);
+  const int lo_last = __builtin_amdgcn_readfirstlane(off[max(upper_index(off, nb, r1 - 1) - a.j, 0)]);
   const int win0 = lo_first / kKeyTile;
   const int win1 = (r1 + kKeyTile - 1) / kKeyTile;
   int nsink = 0;
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256) void k_rows_f32(PrefillArgs a) {
     qr[i] = rot_lo(q[i], q[i + H], c, s) * a.q_scale;
     qr[i + H] = rot_hi(q[i], q[i + H], c, s) * a.q_scale;
   }
-  const int32_t* off = a.offsets;
+  const int32_t* off = a.n_inline ? kernarg_ints(offsetof(PrefillArgs, inl)) : a.offsets;
   const int sink_end = a.sink ? off[1] : 0;
   const int lo_t = off[max(upper_index(off, a.n_blocks, t) - a.j, 0)];
   const float* k = static_cast<const float*>(a.k_tiles) + (int64_t)g * D;

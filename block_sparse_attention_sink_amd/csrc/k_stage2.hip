@@ -46,10 +46,12 @@ __global__ __launch_bounds__(256) void k_gather_bf16(GatherArgs a) {
     rope_cs(base, a.freq.rev[threadIdx.x], tile_c[threadIdx.x], tile_s[threadIdx.x]);
   }
   __syncthreads();
-  const int32_t* st = a.start + (int64_t)b * (a.n_ids + 1);
+  const int32_t* tab = a.n_inline ? kernarg_ints(offsetof(GatherArgs, inl)) : a.tab;
+  const int32_t* st = tab + (int64_t)b * (a.n_ids + 1);
   if (u >= st[a.n_ids]) return;
   const int i = upper_index(st, a.n_ids, u);
-  const int64_t src_tok = a.src[(int64_t)b * a.n_ids + i] + (u - st[i]);
+  const int32_t* srcs = tab + (int64_t)a.batch * (a.n_ids + 1);
+  const int64_t src_tok = srcs[(int64_t)b * a.n_ids + i] + (u - st[i]);
   float cs[8], sn[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -89,10 +91,12 @@ __global__ __launch_bounds__(256) void k_gather_f32(GatherArgs a) {
   const int b = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (token, pair)
   const int u = (int)(idx / H), i = (int)(idx % H);
-  const int32_t* st = a.start + (int64_t)b * (a.n_ids + 1);
+  const int32_t* tab = a.n_inline ? kernarg_ints(offsetof(GatherArgs, inl)) : a.tab;
+  const int32_t* st = tab + (int64_t)b * (a.n_ids + 1);
   if (u >= st[a.n_ids]) return;
   const int s = upper_index(st, a.n_ids, u);
-  const int64_t src_tok = a.src[(int64_t)b * a.n_ids + s] + (u - st[s]);
+  const int32_t* srcs = tab + (int64_t)a.batch * (a.n_ids + 1);
+  const int64_t src_tok = srcs[(int64_t)b * a.n_ids + s] + (u - st[s]);
   float c, sn;
   rope_cs(u, a.freq.rev[i], c, sn);
   const float* kp = static_cast<const float*>(a.k_pool);
@@ -142,10 +146,7 @@ __global__ __launch_bounds__(256) void k_new_kv_f32(NewKVArgs a) {
 // pointer, so no private copy is made) or in device memory.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ const int32_t* seg_block(const QueryArgs& a) {
-  if (a.n_inline)
-    return reinterpret_cast<const int32_t*>((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                                            offsetof(QueryArgs, inl));
-  return a.meta;
+  return a.n_inline ? kernarg_ints(offsetof(QueryArgs, inl)) : a.meta;
 }
 
 // ---------------------------------------------------------------------------

@@ -18,7 +18,7 @@ __all__ = [
     "dbsa_gather_rope",
     "dbsa_query_attn", "dbsa_query_attn_gathered", "dbsa_workspace_bytes", "dbsa_version",
     "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "OP_GATHER_SPANS",
-    "OP_QUERY_SPANS", "SYMBOLS", "dbsa_gather_rope_spans", "dbsa_query_attn_spans", "llama31_inv_freq",
+    "OP_QUERY_SPANS", "SYMBOLS", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so")
@@ -112,23 +112,6 @@ def attn_t(n_q_heads, n_kv_heads, head_dim, dtype, theta, scale=None) -> AttnT:
     return a
 
 
-def llama31_inv_freq(theta: float, head_dim: int, factor: float = 8.0,
-                     low_freq_factor: float = 1.0, high_freq_factor: float = 4.0,
-                     original_context: int = 8192) -> np.ndarray:
-    """Frequency-scaled RoPE table of the Llama-3.1 models (radians per
-    position): frequencies whose wavelength is below original_context /
-    high_freq_factor are kept, those above original_context / low_freq_factor
-    are divided by `factor`, and the band between is blended linearly in
-    original_context / wavelength.  Pass the result as `theta`."""
-    w = theta ** (-(2.0 * np.arange(head_dim // 2, dtype=np.float64)) / head_dim)
-    wavelen = 2.0 * np.pi / w
-    lo_wl = original_context / low_freq_factor
-    hi_wl = original_context / high_freq_factor
-    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
-    blended = (1.0 - smooth) * w / factor + smooth * w
-    return np.where(wavelen < hi_wl, w, np.where(wavelen > lo_wl, w / factor, blended))
-
-
 class Blocks:
     """Keeps the host block_lens array alive for the call."""
 
@@ -174,11 +157,16 @@ def _stream(device) -> int:
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device):
-    """Per-device workspace (at least 1 MiB), grown on demand (calls on one
-    stream are ordered)."""
+def _workspace(nbytes: int, device, stream: int):
+    """Workspace of at least `nbytes` (and 1 MiB) for calls on `stream`.
+
+    One workspace per (device, stream): calls on one stream are ordered, so
+    they may share it, while calls on two streams may overlap and must not.
+    The buffer is allocated on that stream (the current one), so when a
+    larger one replaces it the caching allocator reuses the old memory only
+    for work ordered after the calls that used it."""
     import torch
-    key = str(device)
+    key = (str(device), int(stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -186,17 +174,19 @@ def _workspace(nbytes: int, device):
     return ws
 
 
-def _run(device, call, need):
-    """call(ws_ptr, ws_bytes) with the device's cached workspace.  A call that
-    returns DBSA_ENOSPC has enqueued nothing: the workspace grows to need()
-    bytes and the call is made once more."""
-    ws = _ws_cache.get(str(device))
-    if ws is None:
-        ws = _workspace(0, device)
+def _run(device, stream, call, need):
+    """call(ws_ptr, ws_bytes) with the cached workspace of (device, stream).
+
+    DBSA_ENOSPC means nothing was enqueued.  Only when the workspace itself
+    is too small (need() exceeds it) does it grow and the call run once more;
+    every other ENOSPC (cache, context or output capacity) is raised."""
+    ws = _workspace(0, device, stream)
     rc = call(ws.data_ptr(), ws.numel())
     if rc == ENOSPC:
-        ws = _workspace(need(), device)
-        rc = call(ws.data_ptr(), ws.numel())
+        n = need()
+        if n > ws.numel():
+            ws = _workspace(n, device, stream)
+            rc = call(ws.data_ptr(), ws.numel())
     _check(rc)
 
 
@@ -229,12 +219,39 @@ def dbsa_workspace_bytes(op, n_q_heads, n_kv_heads, head_dim, dtype, theta=1e4, 
     return int(n)
 
 
+def _shape(t, name: str, want) -> None:
+    """Raise EINVAL (before anything reaches the library) unless tensor `t`
+    has len(want) dimensions and every entry of `want` that is not None."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = ", ".join("*" if w is None else str(w) for w in want)
+        raise DbsaError(EINVAL, f"{name} has shape {list(got)}, expected [{shown}]")
+
+
+def _total_tokens(block_lens) -> int:
+    return int(np.sum(np.asarray(block_lens, dtype=np.int64)))
+
+
+def _pool_shape(k_pool, v_pool, hkv: int, d: int, min_tokens: int) -> None:
+    _shape(k_pool, "k_pool", (None, hkv, d))
+    _shape(v_pool, "v_pool", tuple(k_pool.shape))
+    if k_pool.shape[0] < min_tokens:
+        raise DbsaError(EINVAL, f"k_pool holds {k_pool.shape[0]} tokens, the blocks need "
+                                f"{min_tokens}")
+
+
 def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=None):
-    """Stage-1 block-sparse prefill of one layer; returns O [N, Hq, d]."""
+    """Stage-1 block-sparse prefill of one layer: q [N, Hq, d], k, v [N, Hkv, d]
+    with N = sum(block_lens); returns O [N, Hq, d]."""
     import torch
     lib = load()
+    _shape(q, "q", (_total_tokens(block_lens), None, None))
     n, hq, d = q.shape
+    _shape(k, "k", (n, None, d))
     hkv = k.shape[1]
+    _shape(v, "v", (n, hkv, d))
+    if out is not None:
+        _shape(out, "out", (n, hq, d))
     dt = _dtype_code(q)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     b = Blocks(block_lens, sink, j)
@@ -243,7 +260,8 @@ def dbsa_prefill(q, k, v, block_lens, sink: int, j: int, theta, scale=None, out=
     args = (ctypes.byref(a), ctypes.byref(b.t), _ptr(q, "q"), _ptr(k, "k", q.dtype),
             _ptr(v, "v", q.dtype), _ptr(out, "out", q.dtype))
     st = _stream(q.device)
-    _run(q.device, lambda wp, wn: lib.dbsa_prefill(*args, wp, wn, st), lambda: _need(OP_PREFILL, a, b))
+    _run(q.device, st, lambda wp, wn: lib.dbsa_prefill(*args, wp, wn, st),
+         lambda: _need(OP_PREFILL, a, b))
     return out
 
 
@@ -257,13 +275,17 @@ def dbsa_prefill_layers(q, k, v, block_lens, sink: int, j: int, theta, scale=Non
     ql = q if q.dim() == 4 else q.unsqueeze(0)
     kl = k if k.dim() == 4 else k.unsqueeze(0)
     vl = v if v.dim() == 4 else v.unsqueeze(0)
-    _, n, hq, d = ql.shape
+    n = _total_tokens(block_lens)
+    _shape(ql, "q", (None, n, None, None))
+    _, _, hq, d = ql.shape
+    _shape(kl, "k", (None, n, None, d))
     hkv = kl.shape[2]
+    _shape(vl, "v", (kl.shape[0], n, hkv, d))
     for name, t in (("q", ql), ("k", kl), ("v", vl)):
         if t.shape[0] not in (1, n_layers) or not t.is_contiguous():
             raise DbsaError(EINVAL, f"{name}: {n_layers} layers (or one shared), contiguous")
-    if kl.shape[0] != vl.shape[0]:
-        raise DbsaError(EINVAL, "k and v must have the same number of layers")
+    if out is not None:
+        _shape(out, "out", (n_layers, n, hq, d))
     dt = _dtype_code(q)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     b = Blocks(block_lens, sink, j)
@@ -274,18 +296,28 @@ def dbsa_prefill_layers(q, k, v, block_lens, sink: int, j: int, theta, scale=Non
             _ptr(kl, "k", q.dtype), _ptr(vl, "v", q.dtype), stride(kl), _ptr(out, "out", q.dtype),
             out[0].numel())
     st = _stream(q.device)
-    _run(q.device, lambda wp, wn: lib.dbsa_prefill_layers(*args, wp, wn, st),
+    _run(q.device, st, lambda wp, wn: lib.dbsa_prefill_layers(*args, wp, wn, st),
          lambda: _need(OP_PREFILL, a, b))
     return out
 
 
 def dbsa_append_block(q_new, k_new, v_new, k_cache, v_cache, block_lens, sink: int, j: int,
                       theta: float, scale=None, out=None):
-    """Encode one new block onto the pool (block_lens = the existing blocks)."""
+    """Encode one new block onto the pool (block_lens = the existing blocks):
+    q_new [L, Hq, d], k_new, v_new [L, Hkv, d]; k_cache, v_cache [cap, Hkv, d]
+    holding the pool's sum(block_lens) tokens (the new ones are written after
+    them); returns O [L, Hq, d]."""
     import torch
     lib = load()
+    _shape(q_new, "q_new", (None, None, None))
     new_len, hq, d = q_new.shape
+    _shape(k_new, "k_new", (new_len, None, d))
     hkv = k_new.shape[1]
+    _shape(v_new, "v_new", (new_len, hkv, d))
+    _shape(k_cache, "k_cache", (None, hkv, d))
+    _shape(v_cache, "v_cache", tuple(k_cache.shape))
+    if out is not None:
+        _shape(out, "out", (new_len, hq, d))
     dt = _dtype_code(q_new)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     b = Blocks(block_lens, sink, j)
@@ -296,39 +328,61 @@ def dbsa_append_block(q_new, k_new, v_new, k_cache, v_cache, block_lens, sink: i
             _ptr(k_cache, "k_cache", q_new.dtype), _ptr(v_cache, "v_cache", q_new.dtype),
             int(k_cache.shape[0]), _ptr(out, "out", q_new.dtype))
     st = _stream(q_new.device)
-    _run(q_new.device, lambda wp, wn: lib.dbsa_append_block(*args, wp, wn, st),
+    _run(q_new.device, st, lambda wp, wn: lib.dbsa_append_block(*args, wp, wn, st),
          lambda: _need(OP_APPEND, a, b, rows=new_len))
     return out
+
+
+def _ids2d(ids) -> np.ndarray:
+    return np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
 
 
 def dbsa_gather_rope(k_pool, v_pool, block_lens, ids, theta: float, n_q_heads: Optional[int] = None,
                      capacity: Optional[int] = None, k_out=None, v_out=None, sink: int = 1,
                      j: int = 0):
-    """Gather the selected blocks (ids [batch, n_ids], anchor first) and re-rotate K.
+    """Gather the selected blocks (ids [batch, n_ids], anchor first) of the pool
+    k_pool, v_pool [N, Hkv, d] and re-rotate K.
 
     Returns (k_out, v_out, ctx_len) with k_out/v_out [batch, capacity, Hkv, d].
     """
     import torch
     lib = load()
+    _shape(k_pool, "k_pool", (None, None, None))
     _, hkv, d = k_pool.shape
+    _pool_shape(k_pool, v_pool, hkv, d, _total_tokens(block_lens))
     dt = _dtype_code(k_pool)
     a = attn_t(n_q_heads or hkv, hkv, d, dt, theta)
     b = Blocks(block_lens, sink, j)
-    ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
+    ids = _ids2d(ids)
     batch, n_ids = ids.shape
-    if capacity is None:
-        capacity = _max_selected(block_lens, ids)
     if k_out is None:
+        if capacity is None:
+            capacity = _max_selected(block_lens, ids)
         k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
         v_out = torch.empty_like(k_out)
+    _shape(k_out, "k_out", (batch, None, hkv, d))
+    _shape(v_out, "v_out", tuple(k_out.shape))
     ctx = np.zeros(batch, dtype=np.int64)
     args = (ctypes.byref(a), ctypes.byref(b.t), _addr(ids), n_ids, batch, _ptr(k_pool, "k_pool"),
             _ptr(v_pool, "v_pool", k_pool.dtype), _ptr(k_out, "k_out", k_pool.dtype),
             _ptr(v_out, "v_out", k_pool.dtype), int(k_out.shape[1]), _addr(ctx))
     st = _stream(k_pool.device)
-    _run(k_pool.device, lambda wp, wn: lib.dbsa_gather_rope(*args, wp, wn, st),
+    _run(k_pool.device, st, lambda wp, wn: lib.dbsa_gather_rope(*args, wp, wn, st),
          lambda: _need(OP_GATHER, a, b, batch=batch, n_ids=n_ids))
     return k_out, v_out, ctx
+
+
+def _query_shapes(q, k_new, v_new, k_buf, v_buf, buf_name):
+    """Shapes of a Stage-2 call: q [B, n, Hq, d], k_new, v_new [B, n, Hkv, d],
+    context/tail buffers [B, cap, Hkv, d]; returns (B, n, Hq, Hkv, d)."""
+    _shape(q, "q", (None, None, None, None))
+    batch, n_new, hq, d = q.shape
+    _shape(k_new, "k_new", (batch, n_new, None, d))
+    hkv = k_new.shape[2]
+    _shape(v_new, "v_new", (batch, n_new, hkv, d))
+    _shape(k_buf, "k_" + buf_name, (batch, None, hkv, d))
+    _shape(v_buf, "v_" + buf_name, tuple(k_buf.shape))
+    return batch, n_new, hq, hkv, d
 
 
 def dbsa_query_attn(q, k_new, v_new, k_ctx, v_ctx, ctx_len: Sequence[int], theta: float,
@@ -338,8 +392,9 @@ def dbsa_query_attn(q, k_new, v_new, k_ctx, v_ctx, ctx_len: Sequence[int], theta
     tokens' K/V to the cache; the caller advances ctx_len by n_new."""
     import torch
     lib = load()
-    batch, n_new, hq, d = q.shape
-    hkv = k_new.shape[2]
+    batch, n_new, hq, hkv, d = _query_shapes(q, k_new, v_new, k_ctx, v_ctx, "ctx")
+    if out is not None:
+        _shape(out, "out", tuple(q.shape))
     dt = _dtype_code(q)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     ctx = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int64).reshape(batch))
@@ -352,7 +407,7 @@ def dbsa_query_attn(q, k_new, v_new, k_ctx, v_ctx, ctx_len: Sequence[int], theta
             _ptr(v_ctx, "v_ctx", q.dtype), _addr(ctx), int(k_ctx.shape[1]),
             _ptr(out, "out", q.dtype))
     st = _stream(q.device)
-    _run(q.device, lambda wp, wn: lib.dbsa_query_attn(*args, wp, wn, st),
+    _run(q.device, st, lambda wp, wn: lib.dbsa_query_attn(*args, wp, wn, st),
          lambda: _need(OP_QUERY, a, Blocks([1], 1, 0), rows=n_new, batch=batch,
                        max_ctx=int(ctx.max()) + n_new))
     return out
@@ -366,12 +421,16 @@ def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k
     tail_len by n_new."""
     import torch
     lib = load()
-    batch, n_new, hq, d = q.shape
-    hkv = k_new.shape[2]
+    batch, n_new, hq, hkv, d = _query_shapes(q, k_new, v_new, k_tail, v_tail, "tail")
+    _pool_shape(k_pool, v_pool, hkv, d, _total_tokens(block_lens))
+    if out is not None:
+        _shape(out, "out", tuple(q.shape))
     dt = _dtype_code(q)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     b = Blocks(block_lens, 1, 0)
-    ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, dtype=np.int32)))
+    ids = _ids2d(ids)
+    if ids.shape[0] != batch:
+        raise DbsaError(EINVAL, f"ids has {ids.shape[0]} rows, q has batch {batch}")
     n_ids = ids.shape[1]
     tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int64).reshape(batch))
     if out is None:
@@ -384,7 +443,7 @@ def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k
             _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype), _addr(tl),
             int(k_tail.shape[1]), _ptr(out, "out", q.dtype))
     st = _stream(q.device)
-    _run(q.device, lambda wp, wn: lib.dbsa_query_attn_gathered(*args, wp, wn, st),
+    _run(q.device, st, lambda wp, wn: lib.dbsa_query_attn_gathered(*args, wp, wn, st),
          lambda: _need(OP_QUERY_GATHERED, a, b, rows=n_new, batch=batch, n_ids=n_ids,
                        max_ctx=_max_selected(block_lens, ids) + int(tl.max()) + n_new))
     return out
@@ -406,23 +465,27 @@ def dbsa_gather_rope_spans(k_pool, v_pool, span_src, span_len, theta,
     ctx_len) like dbsa_gather_rope."""
     import torch
     lib = load()
+    _shape(k_pool, "k_pool", (None, None, None))
     n_pool, hkv, d = k_pool.shape
+    _pool_shape(k_pool, v_pool, hkv, d, 0)
     dt = _dtype_code(k_pool)
     a = attn_t(n_q_heads or hkv, hkv, d, dt, theta)
     src, ln = _spans(span_src, span_len)
     batch, n_spans = src.shape
-    if capacity is None:
-        capacity = int(max(1, ln.clip(min=0).sum(axis=1).max()))
     if k_out is None:
+        if capacity is None:
+            capacity = int(max(1, ln.clip(min=0).sum(axis=1).max()))
         k_out = torch.empty((batch, capacity, hkv, d), dtype=k_pool.dtype, device=k_pool.device)
         v_out = torch.empty_like(k_out)
+    _shape(k_out, "k_out", (batch, None, hkv, d))
+    _shape(v_out, "v_out", tuple(k_out.shape))
     ctx = np.zeros(batch, dtype=np.int64)
     args = (ctypes.byref(a), _addr(src), _addr(ln), n_spans, batch, int(n_pool),
             _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
             _ptr(k_out, "k_out", k_pool.dtype), _ptr(v_out, "v_out", k_pool.dtype),
             int(k_out.shape[1]), _addr(ctx))
     st = _stream(k_pool.device)
-    _run(k_pool.device, lambda wp, wn: lib.dbsa_gather_rope_spans(*args, wp, wn, st),
+    _run(k_pool.device, st, lambda wp, wn: lib.dbsa_gather_rope_spans(*args, wp, wn, st),
          lambda: _need(OP_GATHER_SPANS, a, None, batch=batch, n_ids=n_spans))
     return k_out, v_out, ctx
 
@@ -434,11 +497,15 @@ def dbsa_query_attn_spans(q, k_new, v_new, k_pool, v_pool, span_src, span_len, k
     dbsa_query_attn_gathered)."""
     import torch
     lib = load()
-    batch, n_new, hq, d = q.shape
-    hkv = k_new.shape[2]
+    batch, n_new, hq, hkv, d = _query_shapes(q, k_new, v_new, k_tail, v_tail, "tail")
+    _pool_shape(k_pool, v_pool, hkv, d, 0)
+    if out is not None:
+        _shape(out, "out", tuple(q.shape))
     dt = _dtype_code(q)
     a = attn_t(hq, hkv, d, dt, theta, scale)
     src, ln = _spans(span_src, span_len)
+    if src.shape[0] != batch:
+        raise DbsaError(EINVAL, f"spans have {src.shape[0]} rows, q has batch {batch}")
     n_spans = src.shape[1]
     tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int64).reshape(batch))
     if out is None:
@@ -451,7 +518,7 @@ def dbsa_query_attn_spans(q, k_new, v_new, k_pool, v_pool, span_src, span_len, k
             _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype), _addr(tl),
             int(k_tail.shape[1]), _ptr(out, "out", q.dtype))
     st = _stream(q.device)
-    _run(q.device, lambda wp, wn: lib.dbsa_query_attn_spans(*args, wp, wn, st),
+    _run(q.device, st, lambda wp, wn: lib.dbsa_query_attn_spans(*args, wp, wn, st),
          lambda: _need(OP_QUERY_SPANS, a, None, rows=n_new, batch=batch, n_ids=n_spans,
                        max_ctx=int(ln.clip(min=0).sum(axis=1).max()) + int(tl.max()) + n_new))
     return out

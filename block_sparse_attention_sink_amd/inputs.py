@@ -19,7 +19,7 @@ from typing import List, Optional
 import numpy as np
 
 __all__ = ["Workload", "workload", "WORKLOADS", "block_lengths_stress", "select_ids",
-           "randn", "PATTERNS"]
+           "randn", "PATTERNS", "llama31_inv_freq"]
 
 # (sink, j) of the ablation patterns [Notes, Ablations > sparse attention pattern]
 # j = -1 stands for "full causal" and is replaced by n_blocks - 1 at use.
@@ -142,3 +142,24 @@ def randn(shape, seed: int, dtype: str = "bf16", device: str = "cpu"):
     g.manual_seed(int(seed))
     x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def llama31_inv_freq(theta: float, head_dim: int, factor: float = 8.0,
+                     low_freq_factor: float = 1.0, high_freq_factor: float = 4.0,
+                     original_context: int = 8192) -> np.ndarray:
+    """A frequency-scaled RoPE table (radians per position) in the form the
+    Llama-3.1 models use, as an input for the RoPE-table option of both the
+    library and the oracle (the method's pages give only theta).
+
+    With w_i = theta^(-2i/d) and wavelength 2 pi / w_i: frequencies whose
+    wavelength is below original_context / high_freq_factor are kept, those
+    above original_context / low_freq_factor are divided by `factor`, and the
+    band between is blended linearly in original_context / wavelength.
+    """
+    w = theta ** (-(2.0 * np.arange(head_dim // 2, dtype=np.float64)) / head_dim)
+    wavelen = 2.0 * np.pi / w
+    lo_wl = original_context / low_freq_factor
+    hi_wl = original_context / high_freq_factor
+    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    blended = (1.0 - smooth) * w / factor + smooth * w
+    return np.where(wavelen < hi_wl, w, np.where(wavelen > lo_wl, w / factor, blended))

@@ -27,11 +27,15 @@
  *    non-OK return nothing has been enqueued and dbsa_last_error() describes
  *    the problem.  DBSA_OK means "enqueued on `stream`" (a hipStream_t, NULL =
  *    the default stream), not "finished": the caller synchronises.
- *  - The library allocates no device memory.  Scratch space is the caller's
- *    workspace `ws` of at least dbsa_workspace_bytes(...) bytes (256-byte
- *    aligned).  A workspace must not be shared by calls that may overlap.
- *    Small per-call tables travel host->device through a pinned staging ring
- *    the library owns (allocated once per device on first use).
+ *  - The library allocates no memory and keeps no state between calls beyond
+ *    the thread-local error text.  Scratch space is the caller's workspace
+ *    `ws` of at least dbsa_workspace_bytes(...) bytes (256-byte aligned).  A
+ *    workspace must not be shared by calls that may overlap.
+ *  - Per-call tables built from the host arrays (block offsets, segment
+ *    lists) travel in the kernel arguments when they fit (512 int32), else
+ *    they are written into the workspace by small copy kernels, 512 int32 per
+ *    launch, on `stream`.  The host never waits and nothing is staged in host
+ *    memory.  Tables above 1 MiB are DBSA_EUNSUPPORTED.
  *  - Calls are thread-safe; error text is thread-local.
  */
 #ifndef DBSA_H

@@ -9,7 +9,7 @@ import torch
 
 from oracle import dbsa_oracle as orc
 from block_sparse_attention_sink_amd import dbsa
-from block_sparse_attention_sink_amd.inputs import randn
+from block_sparse_attention_sink_amd.inputs import llama31_inv_freq, randn
 from tests.helpers import assert_close, assert_bf16_rounding, host64
 
 pytestmark = pytest.mark.gpu
@@ -139,6 +139,16 @@ def test_prefill_one_token_blocks_every_pattern():
         assert_close(got, want, "bf16", f"prefill tiny blocks sink={sink} j={j}")
 
 
+@pytest.mark.parametrize("sink,j", [(1, 2), (0, 5)])
+def test_prefill_many_blocks_table_uploaded(sink, j):
+    """700 blocks: the block-offset table (701 ints) is too big for the kernel
+    arguments and is written into the workspace by copy kernels instead."""
+    rng = np.random.default_rng(91 + j)
+    lens = rng.integers(1, 5, size=700).astype(np.int32)
+    got, want = _run_prefill(lens, 4, 2, 128, "bf16", sink, j, 1e4, seed=93)
+    assert_close(got, want, "bf16", f"prefill 700 blocks sink={sink} j={j}")
+
+
 def test_prefill_repeatable_bitwise():
     rng = np.random.default_rng(77)
     lens = rng.integers(50, 400, size=10).astype(np.int32)
@@ -187,6 +197,49 @@ def test_append_matches_oracle(dtype, sink, j):
     assert_close(host64(o_new), want, dtype, f"append sink={sink} j={j}")
     assert torch.equal(k_cache[:n_old + new_len], k)
     assert torch.equal(v_cache[:n_old + new_len], v)
+
+
+def test_append_onto_many_blocks():
+    """Append onto a 600-block pool (uploaded offset table), sink + previous 2."""
+    rng = np.random.default_rng(95)
+    lens = rng.integers(1, 6, size=600).astype(np.int32)
+    new_len = 150
+    n_old = int(lens.sum())
+    q, k, v = _qkv(n_old + new_len, 4, 2, 128, "bf16", 97)
+    k_cache = torch.zeros((n_old + new_len, 2, 128), dtype=torch.bfloat16, device=DEV)
+    v_cache = torch.zeros_like(k_cache)
+    k_cache[:n_old] = k[:n_old]
+    v_cache[:n_old] = v[:n_old]
+    o_new = dbsa.dbsa_append_block(q[n_old:].contiguous(), k[n_old:].contiguous(),
+                                   v[n_old:].contiguous(), k_cache, v_cache, lens, 1, 2, 5e5)
+    torch.cuda.synchronize()
+    want, _, _, _ = orc.append_block(host64(q[n_old:]), host64(k[n_old:]), host64(v[n_old:]),
+                                     host64(k[:n_old]), host64(v[:n_old]), lens, 1, 2, 5e5)
+    assert_close(host64(o_new), want, "bf16", "append onto 600 blocks")
+
+
+def test_workspace_per_stream():
+    """Calls on two streams get two workspaces (calls that may overlap must
+    not share one), and both results are right while they run side by side."""
+    rng = np.random.default_rng(99)
+    lens = rng.integers(100, 400, size=8).astype(np.int32)
+    n = int(lens.sum())
+    q, k, v = _qkv(n, 8, 2, 128, "bf16", 101)
+    want = dbsa.dbsa_prefill(q, k, v, lens, 1, 2, 1e4).clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for s in (s1, s2):
+        with torch.cuda.stream(s):
+            outs.append(dbsa.dbsa_prefill(q, k, v, lens, 1, 2, 1e4))
+    torch.cuda.synchronize()
+    keys = {key for key in dbsa._ws_cache if key[0] == str(q.device)}
+    assert (str(q.device), s1.cuda_stream) in keys and (str(q.device), s2.cuda_stream) in keys
+    ws1 = dbsa._ws_cache[(str(q.device), s1.cuda_stream)]
+    ws2 = dbsa._ws_cache[(str(q.device), s2.cuda_stream)]
+    assert ws1.data_ptr() != ws2.data_ptr()
+    for o in outs:
+        assert torch.equal(o, want)
 
 
 def test_append_bitwise_equals_prefill_rows_on_tile_boundary():
@@ -347,7 +400,7 @@ def test_query_fused_equals_materialised_bitwise():
 def test_rope_frequency_table_prefill_and_stage2():
     """A frequency-scaled RoPE table (Llama-3.1 style) through prefill and both
     Stage-2 paths, against the oracle given the same table."""
-    table = dbsa.llama31_inv_freq(5e5, 128)
+    table = llama31_inv_freq(5e5, 128)
     rng = np.random.default_rng(29)
     lens = rng.integers(40, 500, size=7).astype(np.int32)
     got, want = _run_prefill(lens, 8, 2, 128, "bf16", 1, 2, table, seed=151)
@@ -507,7 +560,7 @@ def test_spans_with_table_head_dim_64_and_decode():
     rng = np.random.default_rng(59)
     n_pool = 2500
     src, ln = _demo_spans(rng, n_pool, 40, 2, 7, 5, 90)
-    table = dbsa.llama31_inv_freq(5e5, 64)
+    table = llama31_inv_freq(5e5, 64)
     _span_case("bf16", 8, 2, 64, n_pool, src, ln, 9, table, 221)
     # query tokens then single-token steps, each appending to the tail
     hq, hkv, d, theta = 8, 2, 128, 5e5
