@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "dbsa.h"
@@ -833,13 +834,17 @@ int dbsa_query_attn(const dbsa_attn_t* attn, int32_t batch, int32_t n_new, const
 
 namespace {
 
+int scratch_of_current_device(void** out);
+
 // Query tokens over pool spans gathered and re-rotated inside the attention's
-// loads, then the row's tail buffer, then (bf16) the new tokens.
+// loads, then the row's tail buffer, then (bf16) the new tokens.  With
+// static_scratch, `ws` is ignored: the library's scratch array (ws_bytes
+// long) serves as the workspace.
 int query_spans(const dbsa_attn_t* attn, const RowSpans& rs, int32_t batch,
                 const void* k_pool, const void* v_pool, int32_t n_new, const void* q,
                 const void* k_new, const void* v_new, void* k_tail, void* v_tail,
                 const int64_t* tail_len, int64_t tail_capacity, void* o, void* ws,
-                size_t ws_bytes, void* stream) {
+                size_t ws_bytes, void* stream, bool static_scratch = false) {
   if (n_new == 0) return DBSA_OK;
   if (!tail_len) return fail(DBSA_EINVAL, "tail_len is NULL");
   int rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
@@ -896,6 +901,16 @@ int query_spans(const dbsa_attn_t* attn, const RowSpans& rs, int32_t batch,
   query_split(attn, batch, n_new, max_ctx, qp);
   query_layout(attn, batch, sp.tables.size(), qp);
   rc = check_meta(qp.meta_bytes);
+  if (!rc && static_scratch) {
+    // The library's own scratch array: its size is checked before the first
+    // HIP call, then its device address is looked up.
+    if (qp.total > ws_bytes)
+      rc = fail(DBSA_ENOSPC,
+                "this call needs %zu bytes of scratch; the no-allocation entry point has a fixed "
+                "%zu-byte scratch array (fewer query tokens or a smaller batch per call fit)",
+                qp.total, ws_bytes);
+    if (!rc) rc = scratch_of_current_device(&ws);
+  }
   if (!rc) rc = check_ws(ws, ws_bytes, qp.total);
   if (rc) return rc;
   return launch_query_path(attn, batch, n_new, q, k_new, v_new, k_pool, v_pool, k_tail, v_tail,
@@ -943,6 +958,74 @@ int dbsa_query_attn_spans(const dbsa_attn_t* attn, const int32_t* span_src,
   if (n_new == 0) return DBSA_OK;
   return query_spans(attn, rs, batch, k_pool, v_pool, n_new, q, k_new, v_new, k_tail, v_tail,
                      tail_len, tail_capacity, o, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The no-allocation variant of dbsa_query_attn_gathered, for callers that
+// cannot allocate (HIP graph capture, tight serving loops, harnesses that
+// forbid allocation).  Its scratch (split-K partials and the per-call tables
+// that do not fit the kernel arguments) is this file-scope device array: one
+// copy per GPU, loaded with the library's code object and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// handed to kernels.  Calls on one GPU share the array: calls that may overlap
+// on one GPU (two streams) race.  Nothing in it has to start at zero: every
+// call writes each scratch byte it later reads.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(DBSA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DBSA_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign)
+      return fail(DBSA_EHIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DBSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dbsa_query_attn_gathered_noalloc(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                                     const int32_t* ids, int32_t n_ids, int32_t batch,
+                                     const void* k_pool, const void* v_pool, int32_t n_new,
+                                     const void* q, const void* k_new, const void* v_new,
+                                     void* k_tail, void* v_tail, const int64_t* tail_len,
+                                     int64_t tail_capacity, void* o, void* stream) {
+  g_err[0] = 0;
+  std::vector<int32_t> off;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_blocks(blocks, off);
+  if (rc) return rc;
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_new < 0) return fail(DBSA_EINVAL, "n_new must be >= 0");
+  rc = check_ids(ids, n_ids, batch, blocks->n_blocks);
+  if (rc) return rc;
+  if (n_new == 0) return DBSA_OK;
+  return query_spans(attn, spans_of_ids(off, ids, n_ids, batch), batch, k_pool, v_pool, n_new, q,
+                     k_new, v_new, k_tail, v_tail, tail_len, tail_capacity, o, nullptr,
+                     kScratchBytes, stream, true);
 }
 
 }  // extern "C"

@@ -192,6 +192,28 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
                              int64_t tail_capacity, void* o,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the scratch array behind dbsa_query_attn_gathered_noalloc (bytes
+ * per GPU, a file-scope device array of the library, held until the process
+ * ends). */
+#define DBSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* dbsa_query_attn_gathered for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, semantics and results (the same kernels and plan), without a
+ * workspace: the call allocates nothing (no hipMalloc or host allocation) and
+ * uses the library's static scratch array of DBSA_NOALLOC_SCRATCH_BYTES on the
+ * current device.  A call needing more scratch (split-K partials plus the
+ * per-call tables that do not fit the kernel arguments) returns DBSA_ENOSPC
+ * before enqueuing anything.  All calls on one GPU share that array: calls that
+ * may overlap on one GPU (on different streams) race and must not be issued.
+ * The first call on a device looks up the array's device address once. */
+int dbsa_query_attn_gathered_noalloc(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                                     const int32_t* ids, int32_t n_ids, int32_t batch,
+                                     const void* k_pool, const void* v_pool, int32_t n_new,
+                                     const void* q, const void* k_new, const void* v_new,
+                                     void* k_tail, void* v_tail, const int64_t* tail_len,
+                                     int64_t tail_capacity, void* o, void* stream);
+
 /* Stage 2 at example granularity [Notes, Ablations > block-level vs
  * example-level retrieval]: the context is a list of pool token spans (for
  * instance single demonstrations) instead of whole blocks.

@@ -273,3 +273,28 @@ def test_span_validation(lib, fn):
         adj = np.arange(n, dtype=np.int32)
         assert _span_call(lib, fn, [adj], [np.ones(n, np.int32)], pool=4 * n) not in (
             dbsa.EINVAL, dbsa.EUNSUPPORTED)
+
+
+def test_noalloc_entry_checks_before_any_hip_call(lib):
+    """The no-allocation Stage-2 entry validates like dbsa_query_attn_gathered
+    and rejects, on the host, a call whose scratch would exceed its fixed
+    array (255 batch rows x 2 key splits x 128 rows of fp32 partials > 32 MiB)."""
+    a = dbsa.attn_t(4, 1, 128, dbsa.BF16, 1e4)
+    blocks = dbsa.Blocks([200, 200, 200], 1, 2)
+    p32 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p64 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    def call(ids, n_new=32, tail=None, tail_cap=1 << 20):
+        ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, np.int32)))
+        tl = np.zeros(ids.shape[0], np.int64) if tail is None else np.asarray(tail, np.int64)
+        return lib.dbsa_query_attn_gathered_noalloc(
+            ctypes.byref(a), ctypes.byref(blocks.t), p32(ids), ids.shape[1], ids.shape[0], FAKE,
+            FAKE, n_new, FAKE, FAKE, FAKE, FAKE, FAKE, p64(tl), tail_cap, FAKE, None)
+    assert call([[1, 0]]) == dbsa.EINVAL and "anchor" in _err(lib)
+    assert call([[0, 1, 1]]) == dbsa.EINVAL
+    assert call([[0, 1]], n_new=-1) == dbsa.EINVAL
+    assert call([[0, 1]], n_new=0) == dbsa.OK  # nothing to do, nothing enqueued
+    assert call([[0, 1]], tail_cap=16) == dbsa.ENOSPC and "tail_capacity" in _err(lib)
+    big = np.tile(np.array([[0, 1, 2]], np.int32), (255, 1))
+    assert call(big) == dbsa.ENOSPC
+    assert "scratch" in _err(lib) and str(dbsa.NOALLOC_SCRATCH_BYTES) in _err(lib)
