@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdbsa.so")
-SOURCES = ["dbsa_host.hip", "k_stage1.hip", "k_stage2.hip", "k_tables.hip"]
+SOURCES = ["dbsa_host.hip", "k_stage1.hip", "k_stage2.hip", "k_shared.hip", "k_tables.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,7 +27,8 @@ FLAGS = [
 # Kernel files only: scores and probabilities are never NaN (masked scores are
 # -inf, which stays honoured), so max/min need no NaN canonicalisation.  The
 # host file keeps full IEEE semantics for its argument checks.
-KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans"], "k_stage2.hip": ["-fno-honor-nans"]}
+KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans"], "k_stage2.hip": ["-fno-honor-nans"],
+                "k_shared.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):

@@ -241,13 +241,15 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
 // Stage 2 planning.
 // ---------------------------------------------------------------------------
 struct SegPlan {
-  std::vector<int32_t> tables;  // start | src | buf | nseg | pos0 | dst_row
+  std::vector<int32_t> tables;  // start | src | buf | nseg | pos0 | dst_row [| rot]
   int32_t stride = 0;
   size_t o_start = 0, o_src = 0, o_buf = 0, o_nseg = 0, o_pos0 = 0, o_dst = 0;  // int32 index
+  int32_t o_rot = -1;           // index of the rotation offsets, -1: none
 };
 
 struct QueryPlan {
   int32_t rows = 0, row_waves = 4, key_ways = 1, row_groups = 0, n_split = 1, tiles_per_split = 1;
+  bool partials = false;  // rows leave partials (merged by k_combine or k_merge) instead of O
   size_t off_meta = 0, off_po = 0, off_ml = 0, total = 0, meta_bytes = 0;
 };
 
@@ -277,11 +279,15 @@ void query_split(const dbsa_attn_t* a, int32_t batch, int32_t n_new, int64_t max
   }
 }
 
-void query_layout(const dbsa_attn_t* a, int32_t batch, size_t meta_ints, QueryPlan& qp) {
+// Workspace of a query launch: tables, then (split-K, or always when
+// `partials`) the partial O and (m, l) of every row.
+void query_layout(const dbsa_attn_t* a, int32_t batch, size_t meta_ints, QueryPlan& qp,
+                  bool partials = false) {
   qp.meta_bytes = meta_ints * sizeof(int32_t);
   qp.off_meta = 0;
   size_t cur = align_up(qp.meta_bytes);
-  if (qp.n_split > 1) {
+  qp.partials = partials || qp.n_split > 1;
+  if (qp.partials) {
     const size_t prow = (size_t)batch * a->n_kv_heads * qp.n_split * qp.rows;
     qp.off_po = cur;
     cur = align_up(cur + prow * a->head_dim * sizeof(float));
@@ -291,13 +297,14 @@ void query_layout(const dbsa_attn_t* a, int32_t batch, size_t meta_ints, QueryPl
   qp.total = cur;
 }
 
-size_t seg_meta_ints(int32_t batch, int32_t stride) {
-  return (size_t)batch * stride * 3 + (size_t)batch * 3;
+size_t seg_meta_ints(int32_t batch, int32_t stride, bool rot = false) {
+  return (size_t)batch * stride * 3 + (size_t)batch * (rot ? 4 : 3);
 }
 
-void seg_init(SegPlan& sp, int32_t batch, int32_t stride) {
+void seg_init(SegPlan& sp, int32_t batch, int32_t stride, bool rot = false) {
   sp.stride = stride;
-  sp.tables.assign(seg_meta_ints(batch, stride), 0);
+  sp.tables.assign(seg_meta_ints(batch, stride, rot), 0);
+  sp.o_rot = rot ? (int32_t)((size_t)batch * stride * 3 + (size_t)batch * 3) : -1;
   sp.o_start = 0;
   sp.o_src = (size_t)batch * stride;
   sp.o_buf = 2 * (size_t)batch * stride;
@@ -309,7 +316,8 @@ void seg_init(SegPlan& sp, int32_t batch, int32_t stride) {
 int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const void* q,
                       const void* k_new, const void* v_new, const void* k_pool,
                       const void* v_pool, void* k_buf, void* v_buf, int64_t cap, void* o,
-                      const SegPlan& sp, const QueryPlan& qp, void* ws, hipStream_t s) {
+                      const SegPlan& sp, const QueryPlan& qp, void* ws, hipStream_t s,
+                      bool partials_only = false) {
   char* w = static_cast<char*>(ws);
   const bool bf16 = a->dtype == DBSA_BF16;
   // bf16: small tables ride in the kernel arguments (no copy, no extra
@@ -347,8 +355,8 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.k_new = k_new;
   qa.v_new = v_new;
   qa.o = o;
-  qa.part_o = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_po) : nullptr;
-  qa.part_ml = qp.n_split > 1 ? reinterpret_cast<float*>(w + qp.off_ml) : nullptr;
+  qa.part_o = qp.partials ? reinterpret_cast<float*>(w + qp.off_po) : nullptr;
+  qa.part_ml = qp.partials ? reinterpret_cast<float*>(w + qp.off_ml) : nullptr;
   qa.meta = inl ? nullptr : dt;
   qa.seg.o_start = (int32_t)sp.o_start;
   qa.seg.o_src = (int32_t)sp.o_src;
@@ -356,6 +364,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.seg.o_nseg = (int32_t)sp.o_nseg;
   qa.seg.o_pos0 = (int32_t)sp.o_pos0;
   qa.seg.o_dst = (int32_t)sp.o_dst;
+  qa.seg.o_rot = sp.o_rot;
   qa.seg.stride = sp.stride;
   qa.n_inline = inl ? (int32_t)sp.tables.size() : 0;
   if (inl) std::memcpy(qa.inl, sp.tables.data(), sp.tables.size() * sizeof(int32_t));
@@ -374,7 +383,7 @@ int launch_query_path(const dbsa_attn_t* a, int32_t batch, int32_t n_new, const 
   qa.freq = freq;
   e = launch_query(qa, batch, a->head_dim, a->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "launch query");
-  if (qp.n_split > 1) {
+  if (qp.n_split > 1 && !partials_only) {
     CombineArgs ca;
     ca.part_o = qa.part_o;
     ca.part_ml = qa.part_ml;
@@ -477,6 +486,202 @@ int plan_gather(const dbsa_attn_t* a, const dbsa_blocks_t* b, const int32_t* ids
   return DBSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Shared-block schedule of a Stage-2 batch (see k_shared.hip): tables,
+// workspace layout and the tail / new-token pass.
+// ---------------------------------------------------------------------------
+struct SharedPlan {
+  std::vector<int32_t> tab;   // off | bstart | istart | pairs | kslot | ublk | uslot
+  SharedTables t{};
+  int32_t rq = 0, n_pairs = 0;
+  SegPlan sp;                 // tail / new-token pass
+  QueryPlan qp;
+  size_t off_tab = 0, off_k = 0, off_po = 0, off_pl = 0, off_tail = 0, total = 0;
+};
+
+int64_t tiles_of_block(const std::vector<int32_t>& off, int b) {
+  return cdiv(off[b + 1], kKeyTile) - off[b] / kKeyTile;
+}
+
+// Workspace layout (also the bound dbsa_workspace_bytes reports, with every
+// block counted as selected when `ids` is null).
+void shared_layout(const dbsa_attn_t* a, int32_t batch, int32_t n_ids, SharedPlan& p) {
+  const size_t d = (size_t)a->head_dim;
+  p.off_tab = 0;
+  size_t cur = align_up(p.tab.size() * sizeof(int32_t));
+  p.off_k = cur;
+  cur = align_up(cur + (size_t)a->n_kv_heads * p.t.n_slots * kKeyTile * d * 2);
+  const size_t prow = (size_t)batch * a->n_kv_heads * n_ids * p.rq;
+  p.off_po = cur;
+  cur = align_up(cur + prow * d * 2);
+  p.off_pl = cur;
+  cur = align_up(cur + prow * sizeof(float));
+  p.off_tail = cur;
+  p.total = cur + p.qp.total;
+}
+
+// Tables of the shared schedule.  ids == nullptr: sizes only, every block
+// counted as selected (a bound over all ids of this shape).
+int plan_shared(const dbsa_attn_t* a, const std::vector<int32_t>& off, const int32_t* ids,
+                int32_t n_ids, int32_t batch, int32_t n_new, const int64_t* tail_len,
+                SharedPlan& p) {
+  const int nb = (int)off.size() - 1;
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (batch >= (1 << 15) || n_ids >= (1 << 16))
+    return fail(DBSA_EUNSUPPORTED, "batch %d / n_ids %d: at most 32767 rows of 65535 ids", batch,
+                n_ids);
+  if ((int64_t)n_new * G > (1 << 24)) return fail(DBSA_EUNSUPPORTED, "too many query rows");
+  p.rq = n_new * G;
+  std::vector<int32_t> cnt(nb, 0);
+  if (ids) {
+    for (int64_t k = 0; k < (int64_t)batch * n_ids; ++k) cnt[ids[k]]++;
+  } else {
+    std::fill(cnt.begin(), cnt.end(), batch);  // (bound: every block, every row)
+  }
+  p.n_pairs = batch * n_ids;
+  p.t.n_blocks = nb;
+  std::vector<int32_t> bstart(nb + 1, 0), istart(nb + 1, 0), kslot(nb, -1), ublk, uslot(1, 0);
+  int64_t items = 0, slots = 0;
+  for (int b = 0; b < nb; ++b) {
+    bstart[b + 1] = bstart[b] + (ids ? cnt[b] : 0);
+    items += cdiv((int64_t)cnt[b] * p.rq, kPrefillRows);
+    istart[b + 1] = (int32_t)std::min<int64_t>(items, INT32_MAX);
+    if (cnt[b] > 0) {
+      kslot[b] = (int32_t)slots;
+      ublk.push_back(b);
+      slots += tiles_of_block(off, b);
+      uslot.push_back((int32_t)std::min<int64_t>(slots, INT32_MAX));
+    }
+  }
+  if (items * a->n_kv_heads >= INT32_MAX || slots >= INT32_MAX)
+    return fail(DBSA_EUNSUPPORTED, "batch too large for one call");
+  p.t.n_items = (int32_t)items;
+  p.t.n_slots = (int32_t)slots;
+  p.t.n_used = (int32_t)ublk.size();
+  // Table block.
+  p.t.o_off = 0;
+  p.t.o_bstart = nb + 1;
+  p.t.o_istart = 2 * (nb + 1);
+  p.t.o_pairs = 3 * (nb + 1);
+  p.t.o_kslot = p.t.o_pairs + 2 * p.n_pairs;
+  p.t.o_ublk = p.t.o_kslot + nb;
+  p.t.o_uslot = p.t.o_ublk + p.t.n_used;
+  p.tab.assign((size_t)p.t.o_uslot + p.t.n_used + 1, 0);
+  int32_t* tb = p.tab.data();
+  std::copy(off.begin(), off.end(), tb + p.t.o_off);
+  std::copy(bstart.begin(), bstart.end(), tb + p.t.o_bstart);
+  std::copy(istart.begin(), istart.end(), tb + p.t.o_istart);
+  std::copy(kslot.begin(), kslot.end(), tb + p.t.o_kslot);
+  std::copy(ublk.begin(), ublk.end(), tb + p.t.o_ublk);
+  std::copy(uslot.begin(), uslot.end(), tb + p.t.o_uslot);
+  // Tail / new-token pass: per row, the tail buffer (virtual 0 .. tail_len)
+  // and the new tokens after it, turned by the row's gathered length T'.
+  int64_t max_tail = 0;
+  for (int q = 0; q < batch; ++q) max_tail = std::max<int64_t>(max_tail, tail_len ? tail_len[q] : 0);
+  seg_init(p.sp, batch, 3, true);
+  if (ids) {
+    std::vector<int32_t> fill(bstart.begin(), bstart.end() - 1);
+    for (int q = 0; q < batch; ++q) {
+      int64_t tp = 0;
+      for (int i = 0; i < n_ids; ++i) {
+        const int b = ids[(int64_t)q * n_ids + i];
+        tp += off[b + 1] - off[b];
+      }
+      const int64_t pos0 = tp + tail_len[q];
+      if (pos0 + n_new >= (int64_t(1) << 31) - 1024) return fail(DBSA_EINVAL, "context too long");
+      int64_t start = 0;
+      for (int i = 0; i < n_ids; ++i) {
+        const int b = ids[(int64_t)q * n_ids + i];
+        const int64_t shift = pos0 - start + off[b];  // Q turn of token 0 against pool-rotated keys
+        if (shift + n_new >= (int64_t(1) << 31) - 1024)
+          return fail(DBSA_EUNSUPPORTED, "pool position + context length exceeds 2^31");
+        int32_t* pr = tb + p.t.o_pairs + 2 * (size_t)fill[b]++;
+        pr[0] = (q << 16) | i;
+        pr[1] = (int32_t)shift;
+        start += off[b + 1] - off[b];
+      }
+      int32_t* t = p.sp.tables.data();
+      const size_t r3 = (size_t)q * 3;
+      t[p.sp.o_start + r3 + 0] = 0;
+      t[p.sp.o_src + r3 + 0] = 0;
+      t[p.sp.o_buf + r3 + 0] = 1;
+      t[p.sp.o_start + r3 + 1] = (int32_t)tail_len[q];
+      t[p.sp.o_src + r3 + 1] = 0;
+      t[p.sp.o_buf + r3 + 1] = 2;
+      t[p.sp.o_start + r3 + 2] = (int32_t)(tail_len[q] + n_new);
+      t[p.sp.o_nseg + q] = 2;
+      t[p.sp.o_pos0 + q] = (int32_t)tail_len[q];
+      t[p.sp.o_dst + q] = (int32_t)tail_len[q];
+      t[p.sp.o_rot + q] = (int32_t)tp;
+    }
+  }
+  query_split(a, batch, n_new, max_tail + n_new, p.qp);
+  query_layout(a, batch, p.sp.tables.size(), p.qp, true);
+  shared_layout(a, batch, n_ids, p);
+  return check_meta(std::max(p.tab.size(), p.sp.tables.size()) * sizeof(int32_t));
+}
+
+int launch_shared_path(const dbsa_attn_t* a, int32_t batch, int32_t n_ids, int32_t n_new,
+                       int32_t n_tokens, const void* k_pool, const void* v_pool, const void* q,
+                       const void* k_new, const void* v_new, void* k_tail, void* v_tail,
+                       int64_t tail_capacity, void* o, const SharedPlan& p, void* ws,
+                       hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  int rc = upload_ints(p.tab.data(), p.tab.size(), w + p.off_tab, s);
+  if (rc) return rc;
+  const RopeFreq freq = make_freq(a);
+  const int32_t* tab = reinterpret_cast<const int32_t*>(w + p.off_tab);
+  hipError_t e;
+  if (p.t.n_slots > 0) {
+    SharedPackArgs pk;
+    pk.k = k_pool;
+    pk.k_tiles = w + p.off_k;
+    pk.tab = tab;
+    pk.t = p.t;
+    pk.n_tokens = n_tokens;
+    pk.hkv = a->n_kv_heads;
+    pk.freq = freq;
+    e = launch_shared_pack(pk, a->head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "launch shared pack");
+    SharedArgs sa;
+    sa.q = q;
+    sa.k_tiles = w + p.off_k;
+    sa.v = v_pool;
+    sa.part_o = reinterpret_cast<uint16_t*>(w + p.off_po);
+    sa.part_lam = reinterpret_cast<float*>(w + p.off_pl);
+    sa.tab = tab;
+    sa.t = p.t;
+    sa.n_tokens = n_tokens;
+    sa.n_ids = n_ids;
+    sa.n_new = n_new;
+    sa.hq = a->n_q_heads;
+    sa.hkv = a->n_kv_heads;
+    sa.rq = p.rq;
+    sa.q_scale = q_scale_of(a);
+    sa.freq = freq;
+    e = launch_shared(sa, a->head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "launch shared");
+  }
+  rc = launch_query_path(a, batch, n_new, q, k_new, v_new, nullptr, nullptr, k_tail, v_tail,
+                         tail_capacity, o, p.sp, p.qp, w + p.off_tail, s, true);
+  if (rc) return rc;
+  MergeArgs ma;
+  ma.part_o = reinterpret_cast<const uint16_t*>(w + p.off_po);
+  ma.part_lam = reinterpret_cast<const float*>(w + p.off_pl);
+  ma.tail_o = reinterpret_cast<const float*>(w + p.off_tail + p.qp.off_po);
+  ma.tail_ml = reinterpret_cast<const float*>(w + p.off_tail + p.qp.off_ml);
+  ma.o = o;
+  ma.n_ids = n_ids;
+  ma.n_split = p.qp.n_split;
+  ma.rq = p.rq;
+  ma.n_new = n_new;
+  ma.hq = a->n_q_heads;
+  ma.hkv = a->n_kv_heads;
+  e = launch_merge(ma, batch, a->head_dim, s);
+  if (e != hipSuccess) return hip_fail(e, "launch merge");
+  return DBSA_OK;
+}
+
 }  // namespace
 }  // namespace dbsa
 
@@ -514,6 +719,21 @@ size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t
       const size_t mb = (size_t)batch * (2 * (size_t)n_ids + 1) * sizeof(int32_t);
       if (check_meta(mb)) return 0;
       return align_up(mb);
+    }
+    case DBSA_OP_QUERY_BATCHED: {
+      std::vector<int32_t> off;
+      if (check_attn(attn) || check_blocks(blocks, off)) return 0;
+      if (batch < 1 || rows < 1 || n_ids < 1 || max_ctx < rows || max_ctx >= (int64_t(1) << 31)) {
+        fail(DBSA_EINVAL, "need batch, n_new, n_ids >= 1 and n_new <= max_ctx < 2^31");
+        return 0;
+      }
+      if (attn->dtype != DBSA_BF16)
+        return dbsa_workspace_bytes(DBSA_OP_QUERY_GATHERED, attn, blocks, rows, batch, n_ids,
+                                    max_ctx);
+      SharedPlan p;
+      std::vector<int64_t> tl(batch, max_ctx - rows);
+      if (plan_shared(attn, off, nullptr, n_ids, batch, (int32_t)rows, tl.data(), p)) return 0;
+      return p.total;
     }
     case DBSA_OP_QUERY:
     case DBSA_OP_QUERY_GATHERED:
@@ -940,6 +1160,45 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
   return query_spans(attn, spans_of_ids(off, ids, n_ids, batch), batch, k_pool, v_pool, n_new, q,
                      k_new, v_new, k_tail, v_tail, tail_len, tail_capacity, o, ws, ws_bytes,
                      stream);
+}
+
+int dbsa_query_attn_batched(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                            const int32_t* ids, int32_t n_ids, int32_t batch, const void* k_pool,
+                            const void* v_pool, int32_t n_new, const void* q, const void* k_new,
+                            const void* v_new, void* k_tail, void* v_tail,
+                            const int64_t* tail_len, int64_t tail_capacity, void* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<int32_t> off;
+  int rc = check_attn(attn);
+  if (!rc) rc = check_blocks(blocks, off);
+  if (rc) return rc;
+  if (batch < 1) return fail(DBSA_EINVAL, "batch must be >= 1");
+  if (n_new < 0) return fail(DBSA_EINVAL, "n_new must be >= 0");
+  rc = check_ids(ids, n_ids, batch, blocks->n_blocks);
+  if (rc) return rc;
+  if (n_new == 0) return DBSA_OK;
+  if (attn->dtype != DBSA_BF16)  // the float32 path has no shared schedule: same result per row
+    return dbsa_query_attn_gathered(attn, blocks, ids, n_ids, batch, k_pool, v_pool, n_new, q,
+                                    k_new, v_new, k_tail, v_tail, tail_len, tail_capacity, o, ws,
+                                    ws_bytes, stream);
+  if (!tail_len) return fail(DBSA_EINVAL, "tail_len is NULL");
+  rc = check_ptrs({k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o},
+                  "k_pool, v_pool, q, k_new, v_new, k_tail, v_tail, o");
+  if (rc) return rc;
+  for (int b = 0; b < batch; ++b) {
+    if (tail_len[b] < 0) return fail(DBSA_EINVAL, "tail_len[%d] < 0", b);
+    if (tail_len[b] + n_new > tail_capacity)
+      return fail(DBSA_ENOSPC, "tail_len[%d] + n_new = %lld exceeds tail_capacity %lld", b,
+                  (long long)(tail_len[b] + n_new), (long long)tail_capacity);
+  }
+  SharedPlan p;
+  rc = plan_shared(attn, off, ids, n_ids, batch, n_new, tail_len, p);
+  if (!rc) rc = check_ws(ws, ws_bytes, p.total);
+  if (rc) return rc;
+  return launch_shared_path(attn, batch, n_ids, n_new, off.back(), k_pool, v_pool, q, k_new, v_new,
+                            k_tail, v_tail, tail_capacity, o, p, ws,
+                            static_cast<hipStream_t>(stream));
 }
 
 int dbsa_query_attn_spans(const dbsa_attn_t* attn, const int32_t* span_src,

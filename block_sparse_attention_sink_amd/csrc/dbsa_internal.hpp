@@ -99,6 +99,8 @@ struct SegTable {
   int32_t o_nseg;    // [batch]
   int32_t o_pos0;    // [batch] position of new token 0 (= keys before it)
   int32_t o_dst;     // [batch] context-buffer row of new token 0
+  int32_t o_rot;     // [batch] rotation offset added to every position of the row, or -1
+                     // for none (positions are then the virtual positions themselves)
   int32_t stride;
 };
 
@@ -138,8 +140,9 @@ struct QueryArgs {
   void* v_ctx;
   const void* k_new;      // [batch][n_new][hkv][d] (buffer 2)
   const void* v_new;
-  void* o;                // [batch][n_new][hq][d] (when n_split == 1)
-  float* part_o;          // [batch][hkv][n_split][rows][d] (when n_split > 1)
+  void* o;                // [batch][n_new][hq][d] (when part_o is null)
+  float* part_o;          // [batch][hkv][n_split][rows][d] partials, when not null (always
+                          // when n_split > 1; o is then written by a merge kernel)
   float* part_ml;         // [batch][hkv][n_split][rows][2]
   const int32_t* meta;    // table block in device memory (when n_inline == 0)
   SegTable seg;
@@ -155,6 +158,60 @@ struct QueryArgs {
   float q_scale;          // softmax scale * log2(e)
   RopeFreq freq;
   int32_t inl[kInlineInts];
+};
+
+// ---------------------------------------------------------------------------
+// Stage 2 for a batch with block loads shared across the queries that chose
+// each block.  K tiles are rotated once per call at their pool positions; a
+// workgroup takes 256 rows (query, token, head in group) of the queries that
+// selected one block and turns each query's Q by its placement shift (RoPE
+// scores depend only on position differences).  Per (query, block) it leaves
+// a partial: O / l in bf16 and lambda = m + log2(l) (log2 units, softmax scale
+// folded in).  Tables (int32, one block `tab`):
+//   off     [n_blocks + 1]  block start tokens
+//   bstart  [n_blocks + 1]  pairs of block b: pairs[bstart[b] .. bstart[b+1])
+//   istart  [n_blocks + 1]  work items of block b: istart[b] .. istart[b+1]
+//   pairs   [n_pairs][2]    (batch row << 16 | slot of b in the row's ids,
+//                            Q rotation position of the row's token 0)
+//   kslot   [n_blocks]      first K-image slot of block b's tiles (-1: unused)
+//   ublk    [n_used]        blocks selected by some row, ascending
+//   uslot   [n_used + 1]    first K-image slot of each of them
+// ---------------------------------------------------------------------------
+struct SharedTables {
+  int32_t o_off, o_bstart, o_istart, o_pairs, o_kslot, o_ublk, o_uslot;
+  int32_t n_blocks, n_used, n_slots, n_items;
+};
+
+struct SharedPackArgs {
+  const void* k;            // [n_tokens][hkv][d] unrotated pool
+  void* k_tiles;            // [hkv][n_slots][64][d] rotated at pool positions, LDS image
+  const int32_t* tab;
+  SharedTables t;
+  int32_t n_tokens, hkv;
+  RopeFreq freq;
+};
+
+struct SharedArgs {
+  const void* q;            // [batch][n_new][hq][d] unrotated
+  const void* k_tiles;      // from SharedPackArgs
+  const void* v;            // [n_tokens][hkv][d] pool values
+  uint16_t* part_o;         // [batch][hkv][n_ids][rq][d] bf16: O / l
+  float* part_lam;          // [batch][hkv][n_ids][rq]: m + log2(l)
+  const int32_t* tab;
+  SharedTables t;
+  int32_t n_tokens, n_ids, n_new, hq, hkv;
+  int32_t rq;               // rows per (batch row, kv head) = n_new * (hq / hkv)
+  float q_scale;            // softmax scale * log2(e)
+  RopeFreq freq;
+};
+
+struct MergeArgs {
+  const uint16_t* part_o;   // block partials (SharedArgs)
+  const float* part_lam;
+  const float* tail_o;      // the tail / new-token pass: [batch][hkv][n_split][rq][d] O, unnormalised
+  const float* tail_ml;     // [batch][hkv][n_split][rq][2] (m, l)
+  void* o;                  // [batch][n_new][hq][d]
+  int32_t n_ids, n_split, rq, n_new, hq, hkv;
 };
 
 struct CombineArgs {
@@ -176,5 +233,8 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
                         hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int batch, int head_dim, int dtype,
                           hipStream_t stream);
+hipError_t launch_shared_pack(const SharedPackArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_shared(const SharedArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int batch, int head_dim, hipStream_t stream);
 
 }  // namespace dbsa

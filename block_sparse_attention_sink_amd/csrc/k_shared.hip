@@ -1,0 +1,292 @@
+// Stage 2 of DBSA for a batch of queries with block loads shared across the
+// queries that chose each block [Notes, Method > Stage 2, items 1-4].
+//
+// Query q places its selected blocks one after another at positions
+// 0 .. T'_q - 1 and its query tokens after them.  A score depends only on the
+// difference of the two positions RoPE turns by, so instead of rotating every
+// block's keys at each query's placement, the keys are rotated once at their
+// pool positions and each query's rows turn by the placement shift
+//   position(token r) - placement start of block b + pool start of block b.
+// One K/V tile of block b in LDS then serves the rows of every query that
+// selected b; each (query, block) pair leaves a partial softmax, merged later
+// with the query's tail / new-token pass (k_merge).
+//
+// Kernels
+//   k_pack_shared_bf16   rotate the K tiles of every selected block at their
+//                        pool positions into LDS byte images (one slot per
+//                        (block, tile); a tile shared by two blocks is packed
+//                        for each).
+//   k_shared_bf16        flash attention of 256 packed rows (query, token,
+//                        head in GQA group) over one block's tiles: the
+//                        software-pipelined core of the prefill on
+//                        v_mfma_f32_32x32x16_bf16; writes O / l (bf16) and
+//                        m + log2 l per row.
+#include "dbsa_device.hpp"
+
+namespace dbsa {
+
+namespace {
+
+struct SharedTab {
+  const int32_t* off;
+  const int32_t* bstart;
+  const int32_t* istart;
+  const int32_t* pairs;
+  const int32_t* kslot;
+  const int32_t* ublk;
+  const int32_t* uslot;
+};
+
+__device__ __forceinline__ SharedTab shared_tab(const int32_t* tab, const SharedTables& t) {
+  return SharedTab{tab + t.o_off,   tab + t.o_bstart, tab + t.o_istart, tab + t.o_pairs,
+                   tab + t.o_kslot, tab + t.o_ublk,   tab + t.o_uslot};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// K tiles of the selected blocks, rotated at pool positions.  One workgroup
+// per (slot, KV head); slot s belongs to used block u (uslot[u] <= s <
+// uslot[u + 1]) and is its tile kt = off[b] / 64 + (s - uslot[u]).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void k_pack_shared_bf16(SharedPackArgs a) {
+  using Gm = TileGeom<D>;
+  constexpr int CP = D / 16, CR = D / 8;
+  const SharedTab tb = shared_tab(a.tab, a.t);
+  const int slot = blockIdx.x, g = blockIdx.y;
+  const int u = upper_index(tb.uslot, a.t.n_used, slot);
+  const int kt = tb.off[tb.ublk[u]] / kKeyTile + (slot - tb.uslot[u]);
+  const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
+  const int64_t tok = (int64_t)kt * kKeyTile + key;
+  u32x4 k1 = u32x4{0u, 0u, 0u, 0u}, k2 = k1;
+  if (tok < a.n_tokens) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) +
+                                                     (tok * a.hkv + g) * D);
+    k1 = kp[c];
+    k2 = kp[c + CP];
+    rope_rotate_chunk(k1, k2, tok, a.freq, 8 * c);
+  }
+  u32x4* ko = reinterpret_cast<u32x4*>(a.k_tiles) + ((int64_t)g * a.t.n_slots + slot) * (64 * CR);
+  ko[key * CR + Gm::k_phys(key, c)] = k1;
+  ko[key * CR + Gm::k_phys(key, c + CP)] = k2;
+}
+
+// ---------------------------------------------------------------------------
+// Shared-block attention.  Workgroup = 8 wavefronts x 32 packed rows of the
+// pairs (query, slot) that selected block b, chunk `chunk` of them; the
+// workgroup walks the 64-key tiles covering [off[b], off[b + 1]), the first
+// and last masked to the block.  Same LDS rings, loads and pipeline as
+// k_prefill_bf16.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArgs a) {
+  using Gm = TileGeom<D>;
+  constexpr int KS = D / 16;
+  constexpr int NS = kPrefillStages;
+  static_assert(NS == 4, "two tiles in use and two in flight per ring");
+  __shared__ __align__(16) char lds[NS * (Gm::KBYTES + Gm::VBYTES)];
+  char* const kring = lds;
+  char* const vring = lds + NS * Gm::KBYTES;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, col = lane & 31;
+  const SharedTab tb = shared_tab(a.tab, a.t);
+
+  // Work item: (kv head g, item); items are ordered by block, so each XCD
+  // walks consecutive chunks of one block (its K/V tiles stay in that L2).
+  const int lam = xcd_logical(blockIdx.x, gridDim.x);
+  const int g = lam / a.t.n_items;
+  const int item = lam - g * a.t.n_items;
+  const int blk = __builtin_amdgcn_readfirstlane(upper_index(tb.istart, a.t.n_blocks, item));
+  const int chunk = item - __builtin_amdgcn_readfirstlane(tb.istart[blk]);
+  const int p0 = __builtin_amdgcn_readfirstlane(tb.bstart[blk]);
+  const int n_rows = (__builtin_amdgcn_readfirstlane(tb.bstart[blk + 1]) - p0) * a.rq;
+  const int key0 = __builtin_amdgcn_readfirstlane(tb.off[blk]);
+  const int key1 = __builtin_amdgcn_readfirstlane(tb.off[blk + 1]);
+  const int slot0 = __builtin_amdgcn_readfirstlane(tb.kslot[blk]);
+  const int kt0 = key0 / kKeyTile;
+  const int n_tiles = (key1 + kKeyTile - 1) / kKeyTile - kt0;
+
+  // This lane's row: pair (batch row qb, slot of blk in its ids), token r,
+  // head in group h.
+  const int G = a.hq / a.hkv;
+  const int rho = chunk * kPrefillRows + wave * kRowsPerWave + col;
+  const bool live = rho < n_rows;
+  const int pr = live ? rho / a.rq : 0;
+  const int rr = live ? rho - pr * a.rq : 0;
+  const int qi = tb.pairs[2 * (p0 + pr)];
+  const int shift = tb.pairs[2 * (p0 + pr) + 1];
+  const int qb = qi >> 16, qslot = qi & 0xffff;
+  const int r = rr / G;
+  const int head = g * G + (rr - r * G);
+
+  // Q of the row, rotated at its position relative to the block's pool
+  // placement, scale * log2(e) folded in, rounded once to bf16.
+  bf16x8 qb8[KS];
+  {
+    u32x4 raw[KS];
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + (((int64_t)qb * a.n_new + r) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], (int64_t)shift + r, a.freq, 16 * ks + 8 * hh,
+                        a.q_scale);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb8[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+
+  Flash<D> fl;
+  fl.init();
+
+  const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) +
+                       ((int64_t)g * a.t.n_slots + slot0) * Gm::TU4;
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
+  constexpr int NPW = Gm::TU4 / 64 / kPrefillWaves;
+  static_assert(NPW * 64 * kPrefillWaves == Gm::TU4, "tile pieces split evenly over the waves");
+  int kl[NPW], vo[NPW];
+#pragma unroll
+  for (int jj = 0; jj < NPW; ++jj) {
+    const int i = wave + jj * kPrefillWaves;
+    kl[jj] = i * 64 + lane;
+    const int o16 = i * 1024 + lane * 16;
+    const int row = o16 / Gm::ROW;
+    vo[jj] = (row * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8;
+  }
+  const int wsc = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t vtile = (int64_t)kKeyTile * a.hkv * D;
+  auto load_k = [&](int it) {
+    char* st = kring + (it % NS) * Gm::KBYTES;
+    const u32x4* kt = kbase + (int64_t)it * Gm::TU4;
+#pragma unroll
+    for (int jj = 0; jj < NPW; ++jj)
+      dma16s(16u * kl[jj], kt, st + (wsc + jj * kPrefillWaves) * 1024);
+  };
+  auto load_v = [&](int it) {
+    char* st = vring + (it % NS) * Gm::VBYTES;
+    const int kt = kt0 + it;
+    if ((kt + 1) * kKeyTile <= a.n_tokens) {
+      const uint16_t* vt = vsrc + kt * vtile;
+#pragma unroll
+      for (int jj = 0; jj < NPW; ++jj)
+        dma16s(2u * vo[jj], vt, st + (wsc + jj * kPrefillWaves) * 1024);
+    } else {  // last tile of the pool: rows past it repeat its last key (masked)
+#pragma unroll
+      for (int jj = 0; jj < NPW; ++jj) {
+        const int o16 = (wave + jj * kPrefillWaves) * 1024 + lane * 16;
+        const int row = o16 / Gm::ROW;
+        const int64_t tok = min(kt * kKeyTile + row, a.n_tokens - 1);
+        dma16(vsrc + (tok * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8,
+              st + (wsc + jj * kPrefillWaves) * 1024);
+      }
+    }
+  };
+  auto request = [&](int i) {
+    if (i + 3 < n_tiles) load_k(i + 3);
+    if (i + 4 < n_tiles) load_k(i + 4);
+    if (i + 1 < n_tiles) load_v(i + 1);
+    if (i + 2 < n_tiles) load_v(i + 2);
+  };
+  int koff[KS], vbase[D / 32];
+  lane_offsets<D>(lane, koff, vbase);
+
+  // Every row sees the whole block: only the first and last tiles, which
+  // may reach into neighbouring blocks, need the element mask.
+  const auto full_of = [&](int it) {
+    const int k0 = (kt0 + it) * kKeyTile;
+    return k0 >= key0 && k0 + kKeyTile <= key1;
+  };
+  const auto vis_of = [&](int it) {
+    const int k0 = (kt0 + it) * kKeyTile;
+    const int lo = key0 - k0, hi = key1 - k0;
+    return [=](int kr) { return kr >= lo && kr < hi; };
+  };
+  const auto kst = [&](int it) { return kring + (it % NS) * Gm::KBYTES; };
+  const auto vst = [&](int it) { return vring + (it % NS) * Gm::VBYTES; };
+
+  for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
+  load_v(0);
+  wait_vm(0);
+  barrier_nofence();
+  f32x16 s0, s1, n0, n1;
+  bf16x8 prb[4];
+  fl.scores(kst(0), koff, qb8, s0, s1);
+  const auto sync = [&](int i) {
+    wait_vm(0);
+    barrier_nofence();
+    request(i);
+  };
+  sync(0);
+  fl.template pv_head<false>(vst(0), vbase, prb, s0, s1, !full_of(0), vis_of(0));
+  fl.exp_next(kst(1), koff, qb8, s0, s1, prb, n0, n1);
+  for (int i = 1; i < n_tiles; i += 2) {
+    fl.template pv_head<true>(vst(i - 1), vbase, prb, n0, n1, !full_of(i), vis_of(i));
+    fl.exp_next(kst(i + 1), koff, qb8, n0, n1, prb, s0, s1);
+    if (i + 1 >= n_tiles) break;
+    sync(i + 1);
+    fl.template pv_head<true>(vst(i), vbase, prb, s0, s1, !full_of(i + 1), vis_of(i + 1));
+    fl.exp_next(kst(i + 2), koff, qb8, s0, s1, prb, n0, n1);
+  }
+  wait_vm(0);
+  barrier_nofence();
+  fl.pv(vst(n_tiles - 1), vbase, prb);
+
+  // O / l in bf16 and lambda = m + log2(l), staged row by row through the
+  // wave's part of the (idle) K ring so whole 16-byte chunks go out.
+  const float lsum = fl.total();
+  const float inv = live ? 1.0f / lsum : 0.0f;
+  const int64_t prow = (((int64_t)qb * a.hkv + g) * a.n_ids + qslot) * a.rq + rr;
+  if (live && hh == 0) a.part_lam[prow] = fl.m + __builtin_amdgcn_logf(lsum);
+  constexpr int CPR = D / 8;
+  char* const ost = kring + wave * (kRowsPerWave * Gm::ROW);
+  static_assert(kPrefillWaves * kRowsPerWave * Gm::ROW <= NS * Gm::KBYTES, "O fits the K ring");
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 w = {pack_bf16x2(fl.o[m][4 * q4 + 0] * inv, fl.o[m][4 * q4 + 1] * inv),
+                       pack_bf16x2(fl.o[m][4 * q4 + 2] * inv, fl.o[m][4 * q4 + 3] * inv)};
+      const int ch = (m * 4 + q4) ^ (col & (CPR - 1));
+      *reinterpret_cast<u32x2*>(ost + col * Gm::ROW + ch * 16 + hh * 8) = w;
+    }
+  // Destination of each staged row (the rows of one wave may span two pairs).
+  constexpr int RPI = 64 / CPR;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+    const int rr_w = i * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ost + rr_w * Gm::ROW + (ch ^ (rr_w & (CPR - 1))) * 16);
+    const int rho_s = chunk * kPrefillRows + wave * kRowsPerWave + rr_w;
+    if (rho_s < n_rows) {
+      const int pr_s = rho_s / a.rq;
+      const int qi_s = tb.pairs[2 * (p0 + pr_s)];
+      const int64_t row = (((int64_t)(qi_s >> 16) * a.hkv + g) * a.n_ids + (qi_s & 0xffff)) * a.rq +
+                          (rho_s - pr_s * a.rq);
+      *reinterpret_cast<u32x4*>(a.part_o + row * D + ch * 8) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_shared_pack(const SharedPackArgs& a, int head_dim, hipStream_t stream) {
+  const dim3 grid(a.t.n_slots, a.hkv);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(k_pack_shared_bf16<128>, grid, dim3(64 * 8), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_pack_shared_bf16<64>, grid, dim3(64 * 4), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared(const SharedArgs& a, int head_dim, hipStream_t stream) {
+  const dim3 grid(a.t.n_items * a.hkv);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(k_shared_bf16<128>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_shared_bf16<64>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dbsa

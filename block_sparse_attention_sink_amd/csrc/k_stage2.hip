@@ -378,6 +378,8 @@ __global__ __launch_bounds__(64 * (RW * KW + kQueryLoaders), 1) void k_query_bf1
   const int pos0 = tab[a.seg.o_pos0 + b];
   const int dst0 = tab[a.seg.o_dst + b];
   const int qpos = pos0 + r;
+  // Rotation offset of the row: keys and queries turn at virtual position + rot.
+  const int rot = a.seg.o_rot >= 0 ? tab[a.seg.o_rot + b] : 0;
 
   const int nseg = tab[a.seg.o_nseg + b];
   {
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(64 * (RW * KW + kQueryLoaders), 1) void k_query_bf1
       });
       if (wave == NWA && lane < H) {
         float cs, sn;
-        rope_cs((int64_t)(it0 + t) * kKeyTile, fa, cs, sn);
+        rope_cs((int64_t)(it0 + t) * kKeyTile + rot, fa, cs, sn);
         rot_a[t & (NT - 1)][lane] = f32x2{cs, sn};
       }
     };
@@ -575,7 +577,8 @@ __global__ __launch_bounds__(64 * (RW * KW + kQueryLoaders), 1) void k_query_bf1
     for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], qpos, a.freq, 16 * ks + 8 * hh, a.q_scale);
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], (int64_t)qpos + rot, a.freq, 16 * ks + 8 * hh,
+                        a.q_scale);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(64 * (RW * KW + kQueryLoaders), 1) void k_query_bf1
   }
   const float lsum = fl.total();
   if (!live) return;
-  if (a.n_split == 1) {
+  if (a.part_o == nullptr) {
     const float inv = 1.0f / lsum;
     uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
 #pragma unroll
@@ -765,6 +768,64 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Merge of the shared-block schedule: per packed row, the n_ids block
+// partials (O / l in bf16, lambda = m + log2 l) and the n_split partials of
+// the tail / new-token pass (unnormalised O, m, l):
+//   O = (sum_i 2^(lambda_i - M) O_i + sum_s 2^(m_s - M) O_s)
+//       / (sum_i 2^(lambda_i - M) + sum_s 2^(m_s - M) l_s),
+// M the largest exponent among them.  16 threads per row, 8 head dims each.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int rho = blockIdx.x * RPB + threadIdx.x / TPR, c = threadIdx.x % TPR;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (rho >= a.rq) return;
+  const int G = a.hq / a.hkv;
+  const int r = rho / G, head = g * G + rho % G;
+  const int64_t pb = ((int64_t)b * a.hkv + g) * a.n_ids;      // block partial rows
+  const int64_t tb = ((int64_t)b * a.hkv + g) * a.n_split;    // tail partial rows
+  float M = kNegInf;
+  for (int i = 0; i < a.n_ids; ++i) M = fmaxf(M, a.part_lam[(pb + i) * a.rq + rho]);
+  for (int s = 0; s < a.n_split; ++s) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.tail_ml + ((tb + s) * a.rq + rho) * 2);
+    if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+  }
+  float acc[8] = {}, L = 0.0f;
+  for (int i = 0; i < a.n_ids; ++i) {
+    const int64_t row = (pb + i) * a.rq + rho;
+    const float w = __builtin_amdgcn_exp2f(a.part_lam[row] - M);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a.part_o + row * D + 8 * c);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] = __builtin_fmaf(w, bf16_lo(xs[k]), acc[2 * k]);
+      acc[2 * k + 1] = __builtin_fmaf(w, bf16_hi(xs[k]), acc[2 * k + 1]);
+    }
+    L += w;
+  }
+  for (int s = 0; s < a.n_split; ++s) {
+    const int64_t row = (tb + s) * a.rq + rho;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.tail_ml + row * 2);
+    if (!(ml[1] > 0.0f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(a.tail_o + row * D + 8 * c);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(a.tail_o + row * D + 8 * c + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] = __builtin_fmaf(w, x0[k], acc[k]);
+      acc[4 + k] = __builtin_fmaf(w, x1[k], acc[4 + k]);
+    }
+    L = __builtin_fmaf(w, ml[1], L);
+  }
+  const float inv = 1.0f / L;
+  const u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) +
+                            (((int64_t)b * a.n_new + r) * a.hq + head) * D + 8 * c) = out;
+}
+
+// ---------------------------------------------------------------------------
 // float32 query rows: one wavefront per (batch, token, head), one key per lane.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -778,12 +839,13 @@ __global__ __launch_bounds__(256) void k_query_f32(QueryArgs a) {
   const int g = head / (a.hq / a.hkv);
   const int32_t* tab = seg_block(a);
   const int qpos = tab[a.seg.o_pos0 + b] + r;
+  const int rot = a.seg.o_rot >= 0 ? tab[a.seg.o_rot + b] : 0;
   const float* q = static_cast<const float*>(a.q) + (((int64_t)b * a.n_new + r) * a.hq + head) * D;
   float qr[D];
 #pragma unroll
   for (int i = 0; i < H; ++i) {
     float c, s;
-    rope_cs(qpos, a.freq.rev[i], c, s);
+    rope_cs((int64_t)qpos + rot, a.freq.rev[i], c, s);
     qr[i] = rot_lo(q[i], q[i + H], c, s) * a.q_scale;
     qr[i + H] = rot_hi(q[i], q[i + H], c, s) * a.q_scale;
   }
@@ -805,8 +867,8 @@ __global__ __launch_bounds__(256) void k_query_f32(QueryArgs a) {
       const int s = upper_index(sst, nseg, u);
       const int64_t tok = ssrc[s] + (u - sst[s]);
       const float* krow;
-      const bool rot = sbuf[s] == 0;
-      if (rot) {
+      const bool rot_row = sbuf[s] == 0;
+      if (rot_row) {
         krow = kpool + (tok * a.hkv + g) * D;
         vrow = vpool + (tok * a.hkv + g) * D;
       } else {
@@ -818,9 +880,9 @@ __global__ __launch_bounds__(256) void k_query_f32(QueryArgs a) {
 #pragma unroll
       for (int i = 0; i < H; ++i) {
         float x1 = krow[i], x2 = krow[i + H];
-        if (rot) {
+        if (rot_row) {
           float c, sn;
-          rope_cs(u, a.freq.rev[i], c, sn);
+          rope_cs((int64_t)u + rot, a.freq.rev[i], c, sn);
           const float y1 = rot_lo(x1, x2, c, sn), y2 = rot_hi(x1, x2, c, sn);
           x1 = y1;
           x2 = y2;
@@ -915,6 +977,14 @@ hipError_t launch_query(const QueryArgs& a, int batch, int head_dim, int dtype,
   const dim3 grid(a.n_split, a.hkv * a.row_groups, batch);
   if (head_dim == 128) launch_query_d<128>(a, grid, stream);
   else launch_query_d<64>(a, grid, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int batch, int head_dim, hipStream_t stream) {
+  const int rpb = 256 / (head_dim / 8);
+  const dim3 grid((a.rq + rpb - 1) / rpb, a.hkv, batch);
+  if (head_dim == 128) hipLaunchKernelGGL(k_merge<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(k_merge<64>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ __all__ = [
     "dbsa_query_attn", "dbsa_query_attn_gathered", "dbsa_query_attn_gathered_noalloc",
     "dbsa_workspace_bytes", "dbsa_version",
     "OP_PREFILL", "OP_APPEND", "OP_GATHER", "OP_QUERY", "OP_QUERY_GATHERED", "OP_GATHER_SPANS",
-    "OP_QUERY_SPANS", "SYMBOLS", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
+    "OP_QUERY_SPANS", "OP_QUERY_BATCHED", "SYMBOLS", "dbsa_query_attn_batched", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so")
@@ -27,10 +27,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdbsa.so"
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 OP_PREFILL, OP_APPEND, OP_GATHER, OP_QUERY, OP_QUERY_GATHERED = 0, 1, 2, 3, 4
-OP_GATHER_SPANS, OP_QUERY_SPANS = 5, 6
+OP_GATHER_SPANS, OP_QUERY_SPANS, OP_QUERY_BATCHED = 5, 6, 7
 SYMBOLS = ("dbsa_prefill", "dbsa_prefill_layers", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
            "dbsa_query_attn_gathered", "dbsa_query_attn_gathered_noalloc",
-           "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
+           "dbsa_query_attn_batched", "dbsa_gather_rope_spans", "dbsa_query_attn_spans",
            "dbsa_workspace_bytes", "dbsa_last_error", "dbsa_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.dbsa_query_attn.argtypes = [pa, i32, i32, vp, vp, vp, vp, vp, p64, i64, vp, vp, sz, vp]
     lib.dbsa_query_attn_gathered.argtypes = [pa, pb, p32, i32, i32, vp, vp, i32, vp, vp, vp, vp,
                                              vp, p64, i64, vp, vp, sz, vp]
+    lib.dbsa_query_attn_batched.argtypes = [pa, pb, p32, i32, i32, vp, vp, i32, vp, vp, vp, vp,
+                                            vp, p64, i64, vp, vp, sz, vp]
     lib.dbsa_query_attn_gathered_noalloc.argtypes = [pa, pb, p32, i32, i32, vp, vp, i32, vp, vp,
                                                      vp, vp, vp, p64, i64, vp, vp]
     lib.dbsa_gather_rope_spans.argtypes = [pa, p32, p32, i32, i32, i64, vp, vp, vp, vp, i64,
@@ -88,7 +90,7 @@ def load() -> ctypes.CDLL:
     lib.dbsa_version.restype = ctypes.c_char_p
     for name in ("dbsa_prefill", "dbsa_append_block", "dbsa_gather_rope", "dbsa_query_attn",
                  "dbsa_query_attn_gathered", "dbsa_query_attn_gathered_noalloc",
-                 "dbsa_gather_rope_spans", "dbsa_query_attn_spans"):
+                 "dbsa_query_attn_batched", "dbsa_gather_rope_spans", "dbsa_query_attn_spans"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -452,6 +454,41 @@ def dbsa_query_attn_gathered(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k
     _run(q.device, st, lambda wp, wn: lib.dbsa_query_attn_gathered(*args, wp, wn, st),
          lambda: _need(OP_QUERY_GATHERED, a, b, rows=n_new, batch=batch, n_ids=n_ids,
                        max_ctx=_max_selected(block_lens, ids) + int(tl.max()) + n_new))
+    return out
+
+
+def dbsa_query_attn_batched(q, k_new, v_new, k_pool, v_pool, block_lens, ids, k_tail, v_tail,
+                            tail_len: Sequence[int], theta: float, scale=None, out=None):
+    """dbsa_query_attn_gathered with the shared-block schedule: each selected
+    pool block's K/V is loaded once for all the batch rows that chose it.
+    Same arguments and results (up to rounding)."""
+    import torch
+    lib = load()
+    batch, n_new, hq, hkv, d = _query_shapes(q, k_new, v_new, k_tail, v_tail, "tail")
+    _pool_shape(k_pool, v_pool, hkv, d, _total_tokens(block_lens))
+    if out is not None:
+        _shape(out, "out", tuple(q.shape))
+    dt = _dtype_code(q)
+    a = attn_t(hq, hkv, d, dt, theta, scale)
+    b = Blocks(block_lens, 1, 0)
+    ids = _ids2d(ids)
+    if ids.shape[0] != batch:
+        raise DbsaError(EINVAL, f"ids has {ids.shape[0]} rows, q has batch {batch}")
+    n_ids = ids.shape[1]
+    tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int64).reshape(batch))
+    if out is None:
+        out = torch.empty_like(q)
+    if n_new == 0:
+        return out
+    args = (ctypes.byref(a), ctypes.byref(b.t), _addr(ids), n_ids, batch,
+            _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype), n_new, _ptr(q, "q"),
+            _ptr(k_new, "k_new", q.dtype), _ptr(v_new, "v_new", q.dtype),
+            _ptr(k_tail, "k_tail", q.dtype), _ptr(v_tail, "v_tail", q.dtype), _addr(tl),
+            int(k_tail.shape[1]), _ptr(out, "out", q.dtype))
+    st = _stream(q.device)
+    _run(q.device, st, lambda wp, wn: lib.dbsa_query_attn_batched(*args, wp, wn, st),
+         lambda: _need(OP_QUERY_BATCHED, a, b, rows=n_new, batch=batch, n_ids=n_ids,
+                       max_ctx=int(tl.max()) + n_new))
     return out
 
 

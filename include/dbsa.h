@@ -68,7 +68,8 @@ enum {
   DBSA_OP_QUERY = 3,
   DBSA_OP_QUERY_GATHERED = 4,
   DBSA_OP_GATHER_SPANS = 5,
-  DBSA_OP_QUERY_SPANS = 6
+  DBSA_OP_QUERY_SPANS = 6,
+  DBSA_OP_QUERY_BATCHED = 7
 };
 
 /* Shape of one attention layer.
@@ -192,6 +193,28 @@ int dbsa_query_attn_gathered(const dbsa_attn_t* attn, const dbsa_blocks_t* block
                              int64_t tail_capacity, void* o,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Stage 2 for a batch of queries with the block loads shared across the
+ * queries that selected each block [Notes, Method > Stage 2, items 1-4;
+ * Experiments > efficiency comparison: inference cost follows the K/V bytes
+ * read].  Same arguments and results as dbsa_query_attn_gathered (up to
+ * rounding), different schedule: each selected block's unrotated K is rotated
+ * once at its pool positions into the workspace, each K/V tile of a block is
+ * loaded once for the rows of every query that selected it (each query's Q
+ * turned by the block's placement shift, as RoPE scores depend only on
+ * position differences), per-(query, block) partial softmaxes are merged with
+ * a pass over the tail and new tokens.  Suited to large batches (many queries
+ * per block); the workspace grows with batch * n_ids * n_new (partials) plus
+ * the selected blocks' K (see dbsa_workspace_bytes, DBSA_OP_QUERY_BATCHED).
+ * bf16 only in this schedule; DBSA_F32 calls run dbsa_query_attn_gathered.
+ * batch < 32768, n_ids < 65536. */
+int dbsa_query_attn_batched(const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
+                            const int32_t* ids, int32_t n_ids, int32_t batch,
+                            const void* k_pool, const void* v_pool, int32_t n_new,
+                            const void* q, const void* k_new, const void* v_new,
+                            void* k_tail, void* v_tail, const int64_t* tail_len,
+                            int64_t tail_capacity, void* o,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Size of the scratch array behind dbsa_query_attn_gathered_noalloc (bytes
  * per GPU, a file-scope device array of the library, held until the process
  * ends). */
@@ -242,13 +265,14 @@ int dbsa_query_attn_spans(const dbsa_attn_t* attn, const int32_t* span_src,
 /* Workspace bytes the operation needs.
  *   op: DBSA_OP_*.  blocks: the pool (for DBSA_OP_APPEND, the existing pool).
  *   rows: PREFILL ignores it; APPEND: new_len; QUERY / QUERY_GATHERED /
- *   QUERY_SPANS: n_new; GATHER, GATHER_SPANS: ignored.  batch: Stage-2 batch
+ *   QUERY_SPANS / QUERY_BATCHED: n_new; GATHER, GATHER_SPANS: ignored.  batch: Stage-2 batch
  *   (ignored for Stage 1).  n_ids: ids per row (GATHER, QUERY_GATHERED) or
  *   n_spans (GATHER_SPANS, QUERY_SPANS), else ignored.  blocks: ignored by
  *   the span operations (may be NULL).
  *   max_ctx: QUERY: the largest ctx_len[b] + n_new the call will see;
  *   QUERY_GATHERED / QUERY_SPANS: the largest T'_b + tail_len[b] + n_new;
- *   else ignored.
+ *   QUERY_BATCHED: the largest tail_len[b] + n_new (the size returned holds
+ *   for any ids of this shape); else ignored.
  * Returns 0 and sets the error text on invalid arguments. */
 size_t dbsa_workspace_bytes(int op, const dbsa_attn_t* attn, const dbsa_blocks_t* blocks,
                             int64_t rows, int32_t batch, int32_t n_ids, int64_t max_ctx);

@@ -298,3 +298,43 @@ def test_noalloc_entry_checks_before_any_hip_call(lib):
     big = np.tile(np.array([[0, 1, 2]], np.int32), (255, 1))
     assert call(big) == dbsa.ENOSPC
     assert "scratch" in _err(lib) and str(dbsa.NOALLOC_SCRATCH_BYTES) in _err(lib)
+
+
+def test_batched_validation_and_workspace(lib):
+    """The shared-block Stage-2 entry validates like dbsa_query_attn_gathered;
+    its workspace bound covers every id choice of the shape and grows with
+    the batch (partials) but not with the context."""
+    a = _attn()
+    blocks = dbsa.Blocks([100, 37, 250, 3, 64], 1, 2)
+    p32 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p64 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    def call(ids, n_new=4, tail=None, tail_cap=64, ws_bytes=1 << 40):
+        ids = np.ascontiguousarray(np.atleast_2d(np.asarray(ids, np.int32)))
+        tl = np.zeros(ids.shape[0], np.int64) if tail is None else np.asarray(tail, np.int64)
+        return lib.dbsa_query_attn_batched(ctypes.byref(a), ctypes.byref(blocks.t), p32(ids),
+                                           ids.shape[1], ids.shape[0], FAKE, FAKE, n_new, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, p64(tl), tail_cap, FAKE, FAKE,
+                                           ws_bytes, None)
+    assert call([[2, 0]]) == dbsa.EINVAL and "anchor" in _err(lib)
+    assert call([[0, 5]]) == dbsa.EINVAL and "out of range" in _err(lib)
+    assert call([[0, 1, 1]]) == dbsa.EINVAL
+    assert call([[0, 1]], n_new=-1) == dbsa.EINVAL
+    assert call([[0, 1]], n_new=0) == dbsa.OK
+    assert call([[0, 1]], tail=[-1]) == dbsa.EINVAL
+    assert call([[0, 1]], tail=[62]) == dbsa.ENOSPC and "tail_capacity" in _err(lib)
+    assert call([[0, 1]], ws_bytes=1024) == dbsa.ENOSPC and "workspace" in _err(lib)
+    lens = [1024] * 90
+    ws = lambda batch, n_new=48, tail=0: dbsa.dbsa_workspace_bytes(
+        dbsa.OP_QUERY_BATCHED, 32, 8, 128, dbsa.BF16, 5e5, lens, 1, 2, rows=n_new, batch=batch,
+        n_ids=28, max_ctx=tail + n_new)
+    # K of every block (8 heads x 1440 tiles x 16 KiB) + bf16 partials and their weights
+    k_img = 8 * 90 * 16 * 16384
+    part = 64 * 8 * 28 * 192 * (256 + 4)
+    assert k_img + part <= ws(64) < k_img + part + (64 << 20)
+    assert ws(32) < ws(64)
+    # a bound: the size does not depend on which blocks the rows select
+    assert ws(64) == ws(64)
+    with pytest.raises(dbsa.DbsaError):
+        dbsa.dbsa_workspace_bytes(dbsa.OP_QUERY_BATCHED, 32, 8, 128, dbsa.BF16, 5e5, lens, 1, 2,
+                                  rows=48, batch=64, n_ids=0, max_ctx=48)
