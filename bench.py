@@ -11,7 +11,9 @@ workloads, inputs resident in HBM:
   * Stage 2 on the Llama-3.1-8B-shaped 32-layer pool (90 blocks of 50 demos,
     89,568 tokens, 0.125 MiB of K/V per token): for each of the 32 layers, a
     batch of 64 queries, each with the anchor + its own 27 blocks and 48 query
-    tokens -- gather, re-RoPE and query attention (fused into one call).
+    tokens -- gather, re-RoPE and query attention in the shared-block schedule
+    (dbsa_query_attn_batched: each selected block's K/V loaded once for all
+    the queries that chose it).
 Prints one JSON line.  `value` = the stress prefill's FLOP on executed
 (unmasked) key tiles / the prefill's own time (HIP events on the stream it
 runs on).  `roofline` is the prefill call (MFMA-bound; exact visible-pair
@@ -223,12 +225,13 @@ class Stage2Case:
         self.vt = torch.empty_like(self.kt)
         self.work = stage2_work(w.block_lens, w.ids, nn, hq, hkv, d)
 
-    def layer(self, l):
+    def layer(self, l, schedule="per_query"):
         from block_sparse_attention_sink_amd import dbsa
         w = self.w
-        dbsa.dbsa_query_attn_gathered(self.qn, self.kn, self.vn, self.pool_k[l], self.pool_v[l],
-                                      w.block_lens, w.ids, self.kt, self.vt, [0] * w.batch,
-                                      w.theta, out=self.on)
+        fn = dbsa.dbsa_query_attn_batched if schedule == "shared" else \
+            dbsa.dbsa_query_attn_gathered
+        fn(self.qn, self.kn, self.vn, self.pool_k[l], self.pool_v[l], w.block_lens, w.ids,
+           self.kt, self.vt, [0] * w.batch, w.theta, out=self.on)
 
 
 def _events(n):
@@ -255,7 +258,7 @@ def run_main(args, dev):
         if record:
             e[2].record()
         for l in range(L):
-            st2.layer(l)
+            st2.layer(l, "shared")
         if record:
             e[3].record()
             marks.append(e)
@@ -278,9 +281,12 @@ def run_main(args, dev):
     pw, sw = pre.work, st2.work
     value = pw["executed_tile_flop"] / (ms_prefill * 1e-3) / 1e12
     achieved = pw["exact_flop"] / (ms_prefill * 1e-3) / 1e12
-    s2_bytes = sw["bytes_per_query_schedule"]
-    s2_gbs = s2_bytes / (ms_layer * 1e-3) / 1e9
+    s2_tflops = sw["flop"] / (ms_layer * 1e-3) / 1e12
+    s2_unique_gbs = sw["bytes_pool_union"] / (ms_layer * 1e-3) / 1e9
+    s2_perq_gbs = sw["bytes_per_query_schedule"] / (ms_layer * 1e-3) / 1e9
     w5, w4 = pre.w, st2.w
+    # The per-query schedule on the same layer, for comparison.
+    ms_perq = time_calls(lambda: [st2.layer(l, "per_query") for l in range(4)], 3) / 4
 
     llama2 = run_llama2(dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, st2, args.cpu_seconds)
@@ -299,8 +305,8 @@ def run_main(args, dev):
         "data": "synthetic N(0,1) Q/K/V (seeded), no model weights",
         "config": {
             "workload": f"{w5.name} prefill (sink + previous {pre.j}) + append of "
-                        f"{pre.la} tokens; {w4.name} Stage 2 (fused gather + re-RoPE + query "
-                        f"attention, {L} layers)",
+                        f"{pre.la} tokens; {w4.name} Stage 2 (gather + re-RoPE + query "
+                        f"attention, shared-block schedule, {L} layers)",
             "prefill": {"n_tokens": w5.n_tokens, "n_blocks": w5.n_blocks, "q_heads": w5.n_q_heads,
                         "kv_heads": w5.n_kv_heads, "head_dim": w5.head_dim, "sink": pre.sink,
                         "j": pre.j, "rope_theta": w5.theta},
@@ -316,17 +322,18 @@ def run_main(args, dev):
                      "kernel": "dbsa_prefill call (k_pack_bf16 + k_prefill_bf16), stress pool",
                      "ms_per_launch": ms_prefill,
                      "algorithmic_flop_per_launch": pw["exact_flop"]},
-        "roofline_stage2": {"bound": "hbm", "achieved": s2_gbs, "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": s2_gbs / PEAK_HBM_GBS,
+        "roofline_stage2": {"bound": "mfma", "achieved": s2_tflops, "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": s2_tflops / PEAK_BF16_TFLOPS,
                             "traffic": profile_traffic(STAGE2_PROFILE, STAGE2_SOURCES),
-                            "kernel": "dbsa_query_attn_gathered call (k_query_bf16), one layer "
-                                      "of the pool, 64 queries x 48 tokens",
-                            "schedule": "per query: each batch row reads its own gathered "
-                                        "blocks' K/V once",
+                            "kernel": "dbsa_query_attn_batched call (k_pack_shared_bf16 + "
+                                      "k_shared_bf16 + k_query_bf16 + k_merge), one layer of "
+                                      "the pool, 64 queries x 48 tokens",
+                            "schedule": "shared blocks: each selected block's K/V read once for "
+                                        "all queries that chose it; bound by the attention FLOP",
                             "ms_per_launch": ms_layer,
-                            "algorithmic_bytes_per_launch": s2_bytes,
-                            "attention_TFLOP/s": sw["flop"] / (ms_layer * 1e-3) / 1e12,
-                            "pool_union_bytes_per_launch": sw["bytes_pool_union"]},
+                            "algorithmic_flop_per_launch": sw["flop"],
+                            "unique_bytes_per_launch": sw["bytes_pool_union"],
+                            "unique_GB/s": s2_unique_gbs},
         "prefill": {"exact_TFLOP": pw["exact_flop"] / 1e12,
                     "executed_tile_TFLOP": pw["executed_tile_flop"] / 1e12,
                     "tile_tokens_x_keys": pw["tile_tokens_x_keys"],
@@ -334,13 +341,33 @@ def run_main(args, dev):
         "append": {"tokens": pre.la, "ms": ms_append,
                    "TFLOP/s": 4.0 * w5.head_dim * w5.n_q_heads * pre.append_pairs
                    / (ms_append * 1e-3) / 1e12},
-        "stage2": {"ms_all_layers": ms_stage2, "GB/s": s2_gbs, "frac_hbm": s2_gbs / PEAK_HBM_GBS},
+        "stage2": {"ms_all_layers": ms_stage2, "attention_TFLOP/s": s2_tflops,
+                   "per_query_schedule_bytes_GB/s": s2_perq_gbs,
+                   "per_query_schedule": {"ms_per_layer": ms_perq,
+                                          "GB/s": sw["bytes_per_query_schedule"]
+                                          / (ms_perq * 1e-3) / 1e9,
+                                          "note": "dbsa_query_attn_gathered on the same layer: "
+                                                  "each batch row reads its own blocks"}},
         "step_breakdown_ms": {"prefill": ms_prefill, "append": ms_append,
                               "stage2_all_layers": ms_stage2},
         "llama2_layer": llama2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def time_calls(fn, reps):
+    """Median of `reps` timed calls of fn (HIP events on the current stream)."""
+    import torch
+    ts = []
+    for _ in range(reps + 1):
+        a, b = _events(2)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts[1:]))
 
 
 def run_llama2(dev, reps=10):
@@ -450,11 +477,12 @@ def profile_op(dev, op, k, steps, warmup):
     if op in ("prefill", "append"):
         case = PrefillCase(k, dev, with_append=(op == "append"))
         fn = case.prefill if op == "prefill" else case.append
-    elif op == "fused":
+    elif op in ("fused", "batched"):
         case = Stage2Case(k, dev, layers=1)
         if case.w.n_new == 0:
             raise SystemExit(f"workload {k} has no Stage-2 queries")
-        fn = lambda: case.layer(0)
+        sched = "shared" if op == "batched" else "per_query"
+        fn = lambda: case.layer(0, sched)
     else:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -515,10 +543,13 @@ def run_all_workloads(dev):
             o = torch.empty_like(q)
             for nm, (sk, jj) in patterns:
                 jj = len(lens) if jj < 0 else jj
-                flop = 4.0 * d * hq * visible_pairs(lens, sk, jj)
+                pw = prefill_work(lens, sk, jj, hq, hkv, d)
                 ms = timed(lambda: dbsa.dbsa_prefill(q, kk, vv, lens, sk, jj, w.theta, out=o),
                            5 if k != 5 else 3)
-                emit(w.name, f"prefill[{nm}]", ms, flop, "TFLOP/s",
+                # Skipping masked blocks: time should follow the executed tiles.
+                emit(w.name, f"prefill[{nm}]", ms, pw["exact_flop"], "TFLOP/s",
+                     executed_tiles_per_head=pw["executed_tiles_per_head"],
+                     ms_per_1000_tiles=ms / (pw["executed_tiles_per_head"] / 1000.0),
                      note="exact visible-pair flop")
         if w.append_len:
             la = w.append_len
@@ -526,10 +557,16 @@ def run_all_workloads(dev):
             ka = randn((la, hkv, d), 15, dt, dev)
             va = randn((la, hkv, d), 16, dt, dev)
             # Constant cost per new block [Notes, Highlights]: the same block
-            # appended onto pools of 32, 64 and 128 blocks of the stress lengths.
+            # appended onto pools of 32, 64 and 128 blocks of the stress
+            # lengths, with the anchor and the last j blocks (the ones the new
+            # block sees) held at 1024 tokens so that only the pool grows.
             for nb in (32, 64, 128):
-                lens_p = lens[:nb]
+                lens_p = lens[:nb].copy()
+                lens_p[0] = 1024
+                lens_p[nb - w.j:] = 1024
                 npool = int(lens_p.sum())
+                if npool > n:
+                    continue
                 kc = torch.empty((npool + la, hkv, d), dtype=kk.dtype, device=dev)
                 vc = torch.empty_like(kc)
                 kc[:npool].copy_(kk[:npool])
@@ -620,7 +657,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-op", choices=["prefill", "append", "fused", "copy"],
+    ap.add_argument("--profile-op", choices=["prefill", "append", "fused", "batched", "copy"],
                     help="run only this operation --steps times (for rocprofv3); prints timing")
     ap.add_argument("--profile-workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="workload of --profile-op (4: one layer of the pool)")

@@ -150,8 +150,9 @@ struct Stage1Plan {
   int32_t n_tokens = 0;      // keys available (pool + appended block)
   int32_t row0 = 0, row1 = 0;
   int32_t sink_tiles = 0, win_tile0 = 0, win_tile1 = 0, n_slots = 0;
+  int32_t n_split = 1;       // key splits per query tile (short walks: appends)
   // workspace layout
-  size_t off_meta = 0, off_k = 0, total = 0;
+  size_t off_meta = 0, off_k = 0, off_po = 0, off_ml = 0, total = 0;
   size_t meta_bytes = 0;
 };
 
@@ -170,6 +171,15 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
   }
   p.win_tile1 = (int32_t)cdiv(p.n_tokens, kKeyTile);
   p.n_slots = p.sink_tiles + (p.win_tile1 - p.win_tile0);
+  // A short walk over few query tiles (an append) would leave most compute
+  // units idle: cut its key tiles into parts, one workgroup each, aiming at
+  // 256 workgroups and keeping at least 16 tiles per part.
+  p.n_split = 1;
+  if (!whole_pool && a->dtype == DBSA_BF16) {
+    const int64_t wgs = cdiv(p.row1 - p.row0, kPrefillRows) * a->n_q_heads;
+    const int64_t by_len = std::max<int64_t>(1, p.n_slots / 16);
+    p.n_split = (int32_t)std::min<int64_t>({cdiv(256, wgs), by_len, 8});
+  }
   p.meta_bytes = p.off.size() * sizeof(int32_t);
   p.off_meta = 0;
   size_t cur = align_up(p.meta_bytes);
@@ -177,6 +187,13 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
     const size_t tile = (size_t)kKeyTile * a->head_dim * 2;
     p.off_k = cur;
     cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
+  }
+  if (p.n_split > 1) {
+    const size_t prow = (size_t)p.n_split * (p.row1 - p.row0) * a->n_q_heads;
+    p.off_po = cur;
+    cur = align_up(cur + prow * a->head_dim * sizeof(float));
+    p.off_ml = cur;
+    cur = align_up(cur + prow * 2 * sizeof(float));
   }
   p.total = cur;
 }
@@ -215,6 +232,9 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   pa.n_slots = p.n_slots;
   pa.q_scale = q_scale_of(a);
   pa.freq = freq;
+  pa.n_split = p.n_split;
+  pa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(w + p.off_po) : nullptr;
+  pa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(w + p.off_ml) : nullptr;
   if (a->dtype == DBSA_BF16) {
     PackArgs ka;
     ka.k = k;
@@ -234,6 +254,19 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   }
   hipError_t e = launch_prefill(pa, a->head_dim, a->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "launch prefill");
+  if (p.n_split > 1) {  // merge the key splits: rows = (new token, head in group)
+    CombineArgs ca;
+    ca.part_o = pa.part_o;
+    ca.part_ml = pa.part_ml;
+    ca.o = o;
+    ca.n_new = p.row1 - p.row0;
+    ca.hq = a->n_q_heads;
+    ca.hkv = a->n_kv_heads;
+    ca.rows = (p.row1 - p.row0) * (a->n_q_heads / a->n_kv_heads);
+    ca.n_split = p.n_split;
+    e = launch_combine(ca, 1, a->head_dim, a->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "launch combine");
+  }
   return DBSA_OK;
 }
 

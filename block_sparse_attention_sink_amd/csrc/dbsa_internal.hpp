@@ -75,6 +75,14 @@ struct PrefillArgs {
   int32_t sink_tiles, win_tile0, n_slots;  // key-tile slot map (see PackArgs)
   float q_scale;            // softmax scale * log2(e), folded into Q
   RopeFreq freq;
+  // Split keys (n_split > 1, short walks such as an append): the key tiles of
+  // each query tile are cut into n_split consecutive parts, one workgroup
+  // each, which leave unnormalised O and (m, l) per row in part_o / part_ml,
+  // laid out [hkv][n_split][rows * G][d] (row (t - row0) * G + head in group),
+  // for k_combine.
+  int32_t n_split;
+  float* part_o;
+  float* part_ml;
   int32_t n_inline;         // > 0: the offsets are `inl` below
   int32_t inl[kInlineInts];
 };

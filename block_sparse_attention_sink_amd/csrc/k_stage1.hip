@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
 // have separate LDS rings of 4 stages, filled by direct global->LDS loads
 // two tiles at a time (see the loop).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillArgs a) {
   using Gm = TileGeom<D>;
   constexpr int KS = D / 16;
@@ -66,14 +66,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
 
-  // Logical work item: (kv head g, query tile qt, query head within the group).
+  // Logical work item: (kv head g, query tile qt, key split, query head
+  // within the group).  Without SPLIT the walk is whole (n_split == 1), and
+  // the split bookkeeping compiles away.
   const int G = a.hq / a.hkv;
+  const int nsp = SPLIT ? a.n_split : 1;
   const int lam = xcd_logical(blockIdx.x, gridDim.x);
-  const int per_g = a.n_qtiles * G;
+  const int per_g = a.n_qtiles * nsp * G;
   const int g = lam / per_g;
   const int rem = lam - g * per_g;
-  const int qt = rem / G;
-  const int head = g * G + (rem - qt * G);
+  const int qt = rem / (nsp * G);
+  const int rem2 = rem - qt * (nsp * G);
+  const int split = SPLIT ? rem2 / G : 0;
+  const int hig = rem2 - split * G;
+  const int head = g * G + hig;
   const int r0 = a.row0 + qt * kPrefillRows;
   const int r1 = min(r0 + kPrefillRows, a.row1);
   const int t = r0 + wave * kRowsPerWave + col;
@@ -95,7 +101,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int win1 = (r1 + kKeyTile - 1) / kKeyTile;
   int nsink = 0;
   if (a.sink && lo_last > 0) nsink = min((sink_end + kKeyTile - 1) / kKeyTile, win0);
-  const int n_tiles = nsink + (win1 - win0);
+  const int n_all = nsink + (win1 - win0);
+  // This workgroup's part of the walk: tiles [it_lo, it_lo + n_tiles).
+  const int per_split = SPLIT ? (n_all + nsp - 1) / nsp : n_all;
+  const int it_lo = SPLIT ? min(split * per_split, n_all) : 0;
+  const int n_tiles = SPLIT ? min(per_split, n_all - it_lo) : n_all;
 
   // Q: rotate at position t, fold scale * log2(e), round once to bf16.
   bf16x8 qb[KS];
@@ -118,7 +128,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
 
   const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
-  auto tile_of = [&](int it) { return it < nsink ? it : win0 + (it - nsink); };
+  auto tile_of = [&](int it) {
+    if constexpr (SPLIT) it += it_lo;
+    return it < nsink ? it : win0 + (it - nsink);
+  };
   auto slot_of = [&](int kt) {
     return kt < a.sink_tiles ? kt : a.sink_tiles + (kt - a.win_tile0);
   };
@@ -192,6 +205,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const auto kst = [&](int it) { return kring + (it % NS) * Gm::KBYTES; };
   const auto vst = [&](int it) { return vring + (it % NS) * Gm::VBYTES; };
 
+  if (SPLIT && n_tiles <= 0) {  // no keys in this part of the walk: an empty partial
+    const int trow = t - a.row0;
+    if (t < r1 && hh == 0) {
+      const int64_t prow = ((int64_t)g * a.n_split + split) * ((int64_t)(a.row1 - a.row0) * G) +
+                           (int64_t)trow * G + hig;
+      a.part_ml[prow * 2 + 0] = 0.0f;
+      a.part_ml[prow * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+
   // Prologue: K of tiles 0, 1, 2 and V of tile 0, all landed before the
   // scores of tile 0.
   for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
@@ -233,11 +257,30 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   barrier_nofence();
   fl.pv(vst(n_tiles - 1), vbase, pr);
 
+  const float lsum = fl.total();
+  if constexpr (SPLIT) {
+    // Split walk: unnormalised O and (m, l) of the row for k_combine.
+    if (t >= r1) return;
+    const int64_t prow = ((int64_t)g * a.n_split + split) * ((int64_t)(a.row1 - a.row0) * G) +
+                         (int64_t)(t - a.row0) * G + hig;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + m * 32 + q4 * 8 + hh * 4) =
+            f32x4{fl.o[m][4 * q4 + 0], fl.o[m][4 * q4 + 1], fl.o[m][4 * q4 + 2], fl.o[m][4 * q4 + 3]};
+    if (hh == 0) {
+      a.part_ml[prow * 2 + 0] = fl.m;
+      a.part_ml[prow * 2 + 1] = lsum;
+    }
+    return;
+  }
+
   // O = O / l in bf16, staged row by row in the wave's part of the K ring
   // (idle once the last barrier has passed: every K read and K load of the
   // walk is done) so that whole 16-byte chunks of a row go out together;
   // chunks are XOR-swizzled by row against LDS bank conflicts.
-  const float lsum = fl.total();
   const float inv = t < r1 ? 1.0f / lsum : 0.0f;
   constexpr int CPR = D / 8;  // 16-byte chunks per output row
   char* const ost = kring + wave * (kRowsPerWave * Gm::ROW);
@@ -362,11 +405,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStre
       hipLaunchKernelGGL(k_rows_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid(a.n_qtiles * a.hq);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(k_prefill_bf16<128>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_prefill_bf16<64>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
+  const dim3 grid(a.n_qtiles * a.hq * a.n_split);
+  const dim3 block(64 * kPrefillWaves);
+  if (a.n_split > 1) {
+    if (head_dim == 128) hipLaunchKernelGGL((k_prefill_bf16<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_prefill_bf16<64, true>), grid, block, 0, stream, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((k_prefill_bf16<128, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_prefill_bf16<64, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  constexpr int TPR = D / 8, RPB = 256 / TPR, U = 4;
   const int rho = blockIdx.x * RPB + threadIdx.x / TPR, c = threadIdx.x % TPR;
   const int g = blockIdx.y, b = blockIdx.z;
   if (rho >= a.rq) return;
@@ -785,38 +785,53 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   const int r = rho / G, head = g * G + rho % G;
   const int64_t pb = ((int64_t)b * a.hkv + g) * a.n_ids;      // block partial rows
   const int64_t tb = ((int64_t)b * a.hkv + g) * a.n_split;    // tail partial rows
-  float M = kNegInf;
-  for (int i = 0; i < a.n_ids; ++i) M = fmaxf(M, a.part_lam[(pb + i) * a.rq + rho]);
-  for (int s = 0; s < a.n_split; ++s) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.tail_ml + ((tb + s) * a.rq + rho) * 2);
-    if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
-  }
-  float acc[8] = {}, L = 0.0f;
-  for (int i = 0; i < a.n_ids; ++i) {
-    const int64_t row = (pb + i) * a.rq + rho;
-    const float w = __builtin_amdgcn_exp2f(a.part_lam[row] - M);
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a.part_o + row * D + 8 * c);
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+  // One pass, online: the running maximum M only moves up; when it does, the
+  // sums so far are rescaled.  U partials are loaded before they are used.
+  float M = kNegInf, L = 0.0f, acc[8] = {};
+  auto add = [&](float lam, float wl, const float (&x)[8]) {
+    if (lam > M) {
+      const float sc = __builtin_amdgcn_exp2f(M - lam);
+      L *= sc;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[2 * k] = __builtin_fmaf(w, bf16_lo(xs[k]), acc[2 * k]);
-      acc[2 * k + 1] = __builtin_fmaf(w, bf16_hi(xs[k]), acc[2 * k + 1]);
+      for (int k = 0; k < 8; ++k) acc[k] *= sc;
+      M = lam;
     }
-    L += w;
+    const float w = __builtin_amdgcn_exp2f(lam - M);
+    L = __builtin_fmaf(w, wl, L);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
+  };
+  for (int i0 = 0; i0 < a.n_ids; i0 += U) {
+    float lam[U];
+    u32x4 xs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u, a.n_ids - 1);
+      const int64_t row = (pb + i) * a.rq + rho;
+      lam[u] = i0 + u < a.n_ids ? a.part_lam[row] : kNegInf;
+      xs[u] = *reinterpret_cast<const u32x4*>(a.part_o + row * D + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u >= a.n_ids) break;
+      const uint32_t w4[4] = {xs[u].x, xs[u].y, xs[u].z, xs[u].w};
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_lo(w4[k]);
+        x[2 * k + 1] = bf16_hi(w4[k]);
+      }
+      add(lam[u], 1.0f, x);  // O / l with weight 2^(m + log2 l)
+    }
   }
   for (int s = 0; s < a.n_split; ++s) {
     const int64_t row = (tb + s) * a.rq + rho;
     const f32x2 ml = *reinterpret_cast<const f32x2*>(a.tail_ml + row * 2);
     if (!(ml[1] > 0.0f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(a.tail_o + row * D + 8 * c);
     const f32x4 x1 = *reinterpret_cast<const f32x4*>(a.tail_o + row * D + 8 * c + 4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k] = __builtin_fmaf(w, x0[k], acc[k]);
-      acc[4 + k] = __builtin_fmaf(w, x1[k], acc[4 + k]);
-    }
-    L = __builtin_fmaf(w, ml[1], L);
+    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    add(ml[0], ml[1], x);  // unnormalised O with weight 2^m, sum l
   }
   const float inv = 1.0f / L;
   const u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),

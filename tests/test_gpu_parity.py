@@ -199,6 +199,27 @@ def test_append_matches_oracle(dtype, sink, j):
     assert torch.equal(v_cache[:n_old + new_len], v)
 
 
+@pytest.mark.parametrize("j", [2, 8])
+def test_append_split_keys(j):
+    """An append with few query tiles and a long window: its key tiles are cut
+    into parts (one workgroup each) whose partials are merged."""
+    rng = np.random.default_rng(40 + j)
+    lens = rng.integers(500, 700, size=10).astype(np.int32)
+    new_len = 300
+    n_old = int(lens.sum())
+    q, k, v = _qkv(n_old + new_len, 4, 2, 128, "bf16", 131 + j)
+    k_cache = torch.zeros((n_old + new_len, 2, 128), dtype=torch.bfloat16, device=DEV)
+    v_cache = torch.zeros_like(k_cache)
+    k_cache[:n_old] = k[:n_old]
+    v_cache[:n_old] = v[:n_old]
+    o_new = dbsa.dbsa_append_block(q[n_old:].contiguous(), k[n_old:].contiguous(),
+                                   v[n_old:].contiguous(), k_cache, v_cache, lens, 1, j, 5e5)
+    torch.cuda.synchronize()
+    want, _, _, _ = orc.append_block(host64(q[n_old:]), host64(k[n_old:]), host64(v[n_old:]),
+                                     host64(k[:n_old]), host64(v[:n_old]), lens, 1, j, 5e5)
+    assert_close(host64(o_new), want, "bf16", f"append split keys j={j}")
+
+
 def test_append_onto_many_blocks():
     """Append onto a 600-block pool (uploaded offset table), sink + previous 2."""
     rng = np.random.default_rng(95)
