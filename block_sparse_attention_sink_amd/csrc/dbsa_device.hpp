@@ -369,14 +369,18 @@ struct Flash {
     constexpr int H = KS / 2;    // groups per half
     constexpr int PPG = 8 / H;   // score pairs of one half per group
     uint32_t w0[8], w1[8];
-    float sq0[8], sq1[8];
+    // Row sum of the probabilities as they enter P V (rounded to bf16), two
+    // bf16 per v_dot2 against (1, 1), in two chains.
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float la = 0.0f, lb = 0.0f;
     auto fin0 = [&](int u) {
       w0[u] = pack_bf16x2(s0[2 * u], s0[2 * u + 1]);
-      sq0[u] = s0[2 * u] + s0[2 * u + 1];
+      la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[u]), ones, la, false);
     };
     auto fin1 = [&](int u) {
       w1[u] = pack_bf16x2(s1[2 * u], s1[2 * u + 1]);
-      sq1[u] = s1[2 * u] + s1[2 * u + 1];
+      lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[u]), ones, lb, false);
     };
     // Group x: MFMAs of k-steps 2x, 2x + 1 of one accumulator.
     bf16x8 ka[2][2];
@@ -428,14 +432,7 @@ struct Flash {
     }
 #pragma unroll
     for (int e = 0; e < PPG; ++e) fin1((H - 1) * PPG + e);
-    float sq[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) sq[k] = sq0[k] + sq1[k];
-#pragma unroll
-    for (int w = 4; w > 0; w >>= 1)
-#pragma unroll
-      for (int k = 0; k < w; ++k) sq[k] += sq[k + w];
-    l += sq[0];
+    l += la + lb;
     p[0] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
     p[1] = __builtin_bit_cast(bf16x8, u32x4{w0[4], w0[5], w0[6], w0[7]});
     p[2] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
@@ -549,6 +546,77 @@ __device__ __forceinline__ void barrier_nofence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---------------------------------------------------------------------------
+// The software-pipelined tile walk of the 256-row kernels (the prefill and the
+// shared-block Stage-2 kernel).  K tiles and V tiles have separate LDS rings
+// of four stages (tile t in stage t % 4), filled by the caller's load_k /
+// load_v (direct global -> LDS loads, two tiles at a time).  Iteration i
+// computes the softmax of tile i, P V of tile i - 1 and the scores of tile
+// i + 1 (reading K of tile i + 1, V of tile i - 1).  Even iterations start
+// with a barrier: every load requested two iterations earlier has landed
+// (each wave waits for its own, the barrier for all), and the stages of K
+// tiles i - 1, i and V tiles i - 3, i - 2 are refilled for the next two
+// iterations; odd iterations run without one, so the two wavefronts of a SIMD
+// can drift apart.  The loop is unrolled over the four stages: every LDS
+// fragment address is then the lane's base plus a constant, and the score
+// registers alternate instead of being copied.  The last iteration also
+// computes scores of a stale K stage; they are never used.  Leaves O, m, l
+// in fl.
+// ---------------------------------------------------------------------------
+template <int D, typename LoadK, typename LoadV, typename FullOf, typename VisOf>
+__device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char* const vring,
+                                           const int n_tiles, const int (&koff)[D / 16],
+                                           const int (&vbase)[D / 32],
+                                           const bf16x8 (&qb)[D / 16], LoadK&& load_k,
+                                           LoadV&& load_v, FullOf&& full_of, VisOf&& vis_of) {
+  using Gm = TileGeom<D>;
+  static_assert(kPrefillStages == 4, "two tiles in use and two in flight per ring");
+  const auto request = [&](int i) {
+    if (i + 3 < n_tiles) load_k(i + 3);
+    if (i + 4 < n_tiles) load_k(i + 4);
+    if (i + 1 < n_tiles) load_v(i + 1);
+    if (i + 2 < n_tiles) load_v(i + 2);
+  };
+  const auto sync = [&](int i) {
+    wait_vm(0);
+    barrier_nofence();
+    request(i);
+  };
+  const auto ks = [&](int st) { return kring + st * Gm::KBYTES; };
+  const auto vs = [&](int st) { return vring + st * Gm::VBYTES; };
+  // Prologue: K of tiles 0, 1, 2 and V of tile 0, all landed before the
+  // scores of tile 0.
+  for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
+  load_v(0);
+  wait_vm(0);
+  barrier_nofence();
+  f32x16 s0, s1, n0, n1;
+  bf16x8 pr[4];
+  fl.scores(ks(0), koff, qb, s0, s1);
+  sync(0);
+  fl.template pv_head<false>(vs(0), vbase, pr, s0, s1, !full_of(0), vis_of(0));
+  fl.exp_next(ks(1), koff, qb, s0, s1, pr, n0, n1);
+  for (int i = 1; i < n_tiles; i += 4) {
+    fl.template pv_head<true>(vs(0), vbase, pr, n0, n1, !full_of(i), vis_of(i));
+    fl.exp_next(ks(2), koff, qb, n0, n1, pr, s0, s1);
+    if (i + 1 >= n_tiles) break;
+    sync(i + 1);
+    fl.template pv_head<true>(vs(1), vbase, pr, s0, s1, !full_of(i + 1), vis_of(i + 1));
+    fl.exp_next(ks(3), koff, qb, s0, s1, pr, n0, n1);
+    if (i + 2 >= n_tiles) break;
+    fl.template pv_head<true>(vs(2), vbase, pr, n0, n1, !full_of(i + 2), vis_of(i + 2));
+    fl.exp_next(ks(0), koff, qb, n0, n1, pr, s0, s1);
+    if (i + 3 >= n_tiles) break;
+    sync(i + 3);
+    fl.template pv_head<true>(vs(3), vbase, pr, s0, s1, !full_of(i + 3), vis_of(i + 3));
+    fl.exp_next(ks(1), koff, qb, s0, s1, pr, n0, n1);
+  }
+  // P V of the last tile (its V may have been requested by the last barrier).
+  wait_vm(0);
+  barrier_nofence();
+  fl.pv(vs((n_tiles - 1) % kPrefillStages), vbase, pr);
 }
 
 // Workgroup order: the hardware hands consecutive workgroup ids to the 8 XCDs

@@ -183,12 +183,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
       }
     }
   };
-  auto request = [&](int i) {
-    if (i + 3 < n_tiles) load_k(i + 3);
-    if (i + 4 < n_tiles) load_k(i + 4);
-    if (i + 1 < n_tiles) load_v(i + 1);
-    if (i + 2 < n_tiles) load_v(i + 2);
-  };
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 
@@ -203,35 +197,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
     const int lo = key0 - k0, hi = key1 - k0;
     return [=](int kr) { return kr >= lo && kr < hi; };
   };
-  const auto kst = [&](int it) { return kring + (it % NS) * Gm::KBYTES; };
-  const auto vst = [&](int it) { return vring + (it % NS) * Gm::VBYTES; };
-
-  for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
-  load_v(0);
-  wait_vm(0);
-  barrier_nofence();
-  f32x16 s0, s1, n0, n1;
-  bf16x8 prb[4];
-  fl.scores(kst(0), koff, qb8, s0, s1);
-  const auto sync = [&](int i) {
-    wait_vm(0);
-    barrier_nofence();
-    request(i);
-  };
-  sync(0);
-  fl.template pv_head<false>(vst(0), vbase, prb, s0, s1, !full_of(0), vis_of(0));
-  fl.exp_next(kst(1), koff, qb8, s0, s1, prb, n0, n1);
-  for (int i = 1; i < n_tiles; i += 2) {
-    fl.template pv_head<true>(vst(i - 1), vbase, prb, n0, n1, !full_of(i), vis_of(i));
-    fl.exp_next(kst(i + 1), koff, qb8, n0, n1, prb, s0, s1);
-    if (i + 1 >= n_tiles) break;
-    sync(i + 1);
-    fl.template pv_head<true>(vst(i), vbase, prb, s0, s1, !full_of(i + 1), vis_of(i + 1));
-    fl.exp_next(kst(i + 2), koff, qb8, s0, s1, prb, n0, n1);
-  }
-  wait_vm(0);
-  barrier_nofence();
-  fl.pv(vst(n_tiles - 1), vbase, prb);
+  flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb8, load_k, load_v, full_of, vis_of);
 
   // O / l in bf16 and lambda = m + log2(l), staged row by row through the
   // wave's part of the (idle) K ring so whole 16-byte chunks go out.

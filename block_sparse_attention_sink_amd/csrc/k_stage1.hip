@@ -181,14 +181,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
       }
     }
   };
-  // Requests of (even) iteration i: K of tiles i + 3 and i + 4 and V of
-  // tiles i + 1 and i + 2, each when it exists.
-  auto request = [&](int i) {
-    if (i + 3 < n_tiles) load_k(i + 3);
-    if (i + 4 < n_tiles) load_k(i + 4);
-    if (i + 1 < n_tiles) load_v(i + 1);
-    if (i + 2 < n_tiles) load_v(i + 2);
-  };
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 
@@ -202,9 +194,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
     return [=](int kr) { return kr <= tt && (kr >= lt || kr < se); };
   };
-  const auto kst = [&](int it) { return kring + (it % NS) * Gm::KBYTES; };
-  const auto vst = [&](int it) { return vring + (it % NS) * Gm::VBYTES; };
-
   if (SPLIT && n_tiles <= 0) {  // no keys in this part of the walk: an empty partial
     const int trow = t - a.row0;
     if (t < r1 && hh == 0) {
@@ -215,47 +204,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     }
     return;
   }
-
-  // Prologue: K of tiles 0, 1, 2 and V of tile 0, all landed before the
-  // scores of tile 0.
-  for (int i = 0; i < 3 && i < n_tiles; ++i) load_k(i);
-  load_v(0);
-  wait_vm(0);
-  barrier_nofence();
-  f32x16 s0, s1, n0, n1;
-  bf16x8 pr[4];
-  fl.scores(kst(0), koff, qb, s0, s1);
-  // Iteration i computes the softmax of tile i, P V of tile i - 1 and the
-  // scores of tile i + 1 (reading K of tile i + 1, V of tile i - 1).  Even
-  // iterations start with a barrier: every load requested two iterations
-  // earlier has landed (each wave waits for its own, the barrier for all),
-  // and the stages of K tiles i - 1, i and V tiles i - 3, i - 2, which
-  // iterations up to i - 1 read, are refilled for the next two iterations.
-  // Odd iterations run without a barrier, so the two wavefronts of a SIMD
-  // can drift apart.  The last iteration also computes scores, of a stale K
-  // stage; they are never used.
-  const auto sync = [&](int i) {
-    wait_vm(0);
-    barrier_nofence();
-    request(i);
-  };
-  sync(0);
-  fl.template pv_head<false>(vst(0), vbase, pr, s0, s1, !full_of(0), vis_of(0));
-  fl.exp_next(kst(1), koff, qb, s0, s1, pr, n0, n1);
-  // Two iterations per trip (odd, then even) so the score registers
-  // alternate instead of being copied.
-  for (int i = 1; i < n_tiles; i += 2) {
-    fl.template pv_head<true>(vst(i - 1), vbase, pr, n0, n1, !full_of(i), vis_of(i));
-    fl.exp_next(kst(i + 1), koff, qb, n0, n1, pr, s0, s1);
-    if (i + 1 >= n_tiles) break;
-    sync(i + 1);
-    fl.template pv_head<true>(vst(i), vbase, pr, s0, s1, !full_of(i + 1), vis_of(i + 1));
-    fl.exp_next(kst(i + 2), koff, qb, s0, s1, pr, n0, n1);
-  }
-  // P V of the last tile (its V may have been requested by the last barrier).
-  wait_vm(0);
-  barrier_nofence();
-  fl.pv(vst(n_tiles - 1), vbase, pr);
+  flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb, load_k, load_v, full_of, vis_of);
 
   const float lsum = fl.total();
   if constexpr (SPLIT) {
