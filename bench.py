@@ -64,7 +64,7 @@ def visible_pairs(lens, sink, j):
     return total
 
 
-PREFILL_MAX_PACKED_HEADS = 1  # query heads of one KV head sharing a prefill workgroup
+PREFILL_MAX_PACKED_HEADS = 4  # query heads of one KV head sharing a prefill workgroup
 
 
 def prefill_row_tile(hq, hkv):

@@ -151,6 +151,7 @@ struct Stage1Plan {
   int32_t row0 = 0, row1 = 0;
   int32_t sink_tiles = 0, win_tile0 = 0, win_tile1 = 0, n_slots = 0;
   int32_t n_split = 1;       // key splits per query tile (short walks: appends)
+  int32_t pack_log2 = 0;     // query heads of a KV head per workgroup (log2), bf16
   // workspace layout
   size_t off_meta = 0, off_k = 0, off_po = 0, off_ml = 0, total = 0;
   size_t meta_bytes = 0;
@@ -171,12 +172,21 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
   }
   p.win_tile1 = (int32_t)cdiv(p.n_tokens, kKeyTile);
   p.n_slots = p.sink_tiles + (p.win_tile1 - p.win_tile0);
+  // GQA: up to kPrefillPackHeads query heads of one KV head share a
+  // workgroup and each K/V tile it stages (256 rows = tokens x heads).
+  p.pack_log2 = 0;
+  if (a->dtype == DBSA_BF16) {
+    const int G = a->n_q_heads / a->n_kv_heads;
+    while ((2 << p.pack_log2) <= std::min(G, kPrefillPackHeads) && G % (2 << p.pack_log2) == 0)
+      ++p.pack_log2;
+  }
   // A short walk over few query tiles (an append) would leave most compute
   // units idle: cut its key tiles into parts, one workgroup each, aiming at
   // 256 workgroups and keeping at least 16 tiles per part.
   p.n_split = 1;
   if (!whole_pool && a->dtype == DBSA_BF16) {
-    const int64_t wgs = cdiv(p.row1 - p.row0, kPrefillRows) * a->n_q_heads;
+    const int64_t wgs = cdiv(p.row1 - p.row0, kPrefillRows >> p.pack_log2) *
+                        (a->n_q_heads >> p.pack_log2);
     const int64_t by_len = std::max<int64_t>(1, p.n_slots / 16);
     p.n_split = (int32_t)std::min<int64_t>({cdiv(256, wgs), by_len, 8});
   }
@@ -224,7 +234,8 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   pa.q_row0 = q_row0;
   pa.hq = a->n_q_heads;
   pa.hkv = a->n_kv_heads;
-  pa.n_qtiles = (int32_t)cdiv(p.row1 - p.row0, kPrefillRows);
+  pa.pack_log2 = p.pack_log2;
+  pa.n_qtiles = (int32_t)cdiv(p.row1 - p.row0, kPrefillRows >> p.pack_log2);
   pa.n_keys = p.n_tokens;
   pa.v = v;
   pa.sink_tiles = p.sink_tiles;

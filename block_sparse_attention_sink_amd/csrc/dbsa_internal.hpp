@@ -17,6 +17,7 @@ constexpr int kRowsPerWave = 32;  // query rows per wavefront (MFMA N dimension)
 constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
 constexpr int kPrefillStages = 4;  // LDS stages per K ring and per V ring
+constexpr int kPrefillPackHeads = 4;  // most query heads of one KV head per prefill workgroup
 constexpr int kMaxSegments = 1024;  // context segments per batch row in Stage 2
 constexpr int kQueryLoaders = 4;   // Stage-2 wavefronts that load and rotate the tiles
 constexpr int kQueryLead = 3;      // tiles each of their threads keeps in flight
@@ -70,7 +71,9 @@ struct PrefillArgs {
   int32_t row0, row1;       // absolute query rows [row0, row1) of this call
   int32_t q_row0;           // absolute row of q[0] / o[0]
   int32_t hq, hkv;
-  int32_t n_qtiles;         // ceil((row1 - row0) / kPrefillRows)
+  int32_t n_qtiles;         // ceil((row1 - row0) / (kPrefillRows >> pack_log2))
+  int32_t pack_log2;        // 2^pack_log2 query heads of one KV head share a workgroup (and
+                            // every K/V tile it loads): kPrefillRows >> pack_log2 tokens each
   int32_t n_keys;           // keys available (rows of v)
   int32_t sink_tiles, win_tile0, n_slots;  // key-tile slot map (see PackArgs)
   float q_scale;            // softmax scale * log2(e), folded into Q

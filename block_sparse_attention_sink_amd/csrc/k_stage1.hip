@@ -66,23 +66,30 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
 
-  // Logical work item: (kv head g, query tile qt, key split, query head
-  // within the group).  Without SPLIT the walk is whole (n_split == 1), and
-  // the split bookkeeping compiles away.
+  // Logical work item: (kv head g, query tile qt, key split, group of P =
+  // 2^pack_log2 query heads of g).  The workgroup's 256 rows are 256 / P
+  // tokens x P heads: wave w takes head w % P of the group for tokens
+  // 32 (w / P) .. + 31, so one LDS K/V tile serves P heads.  Without SPLIT
+  // the walk is whole (n_split == 1), and the split bookkeeping compiles away.
   const int G = a.hq / a.hkv;
+  const int pl = a.pack_log2, P = 1 << pl;
+  const int HS = G >> pl;  // head groups per KV head
   const int nsp = SPLIT ? a.n_split : 1;
   const int lam = xcd_logical(blockIdx.x, gridDim.x);
-  const int per_g = a.n_qtiles * nsp * G;
+  const int per_g = a.n_qtiles * nsp * HS;
   const int g = lam / per_g;
   const int rem = lam - g * per_g;
-  const int qt = rem / (nsp * G);
-  const int rem2 = rem - qt * (nsp * G);
-  const int split = SPLIT ? rem2 / G : 0;
-  const int hig = rem2 - split * G;
+  const int qt = rem / (nsp * HS);
+  const int rem2 = rem - qt * (nsp * HS);
+  const int split = SPLIT ? rem2 / HS : 0;
+  const int hsub = rem2 - split * HS;
+  const int hig = (hsub << pl) + (wave & (P - 1));
   const int head = g * G + hig;
-  const int r0 = a.row0 + qt * kPrefillRows;
-  const int r1 = min(r0 + kPrefillRows, a.row1);
-  const int t = r0 + wave * kRowsPerWave + col;
+  const int tw = kPrefillRows >> pl;  // tokens per workgroup
+  const int r0 = a.row0 + qt * tw;
+  const int r1 = min(r0 + tw, a.row1);
+  const int wrow = (wave >> pl) * kRowsPerWave;  // this wave's first token, from r0
+  const int t = r0 + wrow + col;
 
   // Visible key intervals [Notes, Method > Stage 1, item 2]:
   // row t sees [lo(t), t] with lo(t) = start of block max(blk(t) - j, 0),
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   for (int i = 0; i < kRowsPerWave / RPI; ++i) {
     const int rr = i * RPI + lane / CPR, ch = lane % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(ost + rr * Gm::ROW + (ch ^ (rr & (CPR - 1))) * 16);
-    const int trow = r0 + wave * kRowsPerWave + rr;
+    const int trow = r0 + wrow + rr;
     if (trow < r1)
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) +
                                 ((int64_t)(trow - a.q_row0) * a.hq + head) * D + ch * 8) = v;
@@ -354,7 +361,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStre
       hipLaunchKernelGGL(k_rows_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid(a.n_qtiles * a.hq * a.n_split);
+  const dim3 grid(a.n_qtiles * (a.hq >> a.pack_log2) * a.n_split);
   const dim3 block(64 * kPrefillWaves);
   if (a.n_split > 1) {
     if (head_dim == 128) hipLaunchKernelGGL((k_prefill_bf16<128, true>), grid, block, 0, stream, a);
