@@ -121,26 +121,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   const int r = rr / G;
   const int head = g * G + (rr - r * G);
 
-  // Q of the row, rotated at its position relative to the block's pool
-  // placement, scale * log2(e) folded in, rounded once to bf16.
-  bf16x8 qb8[KS];
-  {
-    u32x4 raw[KS];
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + (((int64_t)qb * a.n_new + r) * a.hq + head) * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], (int64_t)shift + r, a.freq, 16 * ks + 8 * hh,
-                        a.q_scale);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb8[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-  }
-
-  Flash<D> fl;
-  fl.init();
-
   const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) +
                        ((int64_t)g * a.t.n_slots + slot0) * Gm::TU4;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
@@ -183,6 +163,29 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
       }
     }
   };
+  flash_walk_start(n_tiles, load_k, load_v);
+
+  // Q of the row, rotated at its position relative to the block's pool
+  // placement, scale * log2(e) folded in, rounded once to bf16.
+  bf16x8 qb8[KS];
+  {
+    u32x4 raw[KS];
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + (((int64_t)qb * a.n_new + r) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], (int64_t)shift + r, a.freq, 16 * ks + 8 * hh,
+                        a.q_scale);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb8[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+
+
+  Flash<D> fl;
+  fl.init();
+
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 

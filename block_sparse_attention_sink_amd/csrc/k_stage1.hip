@@ -114,25 +114,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int it_lo = SPLIT ? min(split * per_split, n_all) : 0;
   const int n_tiles = SPLIT ? min(per_split, n_all - it_lo) : n_all;
 
-  // Q: rotate at position t, fold scale * log2(e), round once to bf16.
-  bf16x8 qb[KS];
-  {
-    u32x4 raw[KS];
-    const bool live = t < r1;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)(t - a.q_row0) * a.hq + head) * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], t, a.freq, 16 * ks + 8 * hh, a.q_scale);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-  }
-
-  Flash<D> fl;
-  fl.init();
-
   const u32x4* kbase = reinterpret_cast<const u32x4*>(a.k_tiles) + (int64_t)g * a.n_slots * Gm::TU4;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
   auto tile_of = [&](int it) {
@@ -188,6 +169,38 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
       }
     }
   };
+  if (SPLIT && n_tiles <= 0) {  // no keys in this part of the walk: an empty partial
+    const int trow = t - a.row0;
+    if (t < r1 && hh == 0) {
+      const int64_t prow = ((int64_t)g * a.n_split + split) * ((int64_t)(a.row1 - a.row0) * G) +
+                           (int64_t)trow * G + hig;
+      a.part_ml[prow * 2 + 0] = 0.0f;
+      a.part_ml[prow * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+  flash_walk_start(n_tiles, load_k, load_v);
+
+  // Q: rotate at position t, fold scale * log2(e), round once to bf16.
+  bf16x8 qb[KS];
+  {
+    u32x4 raw[KS];
+    const bool live = t < r1;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)(t - a.q_row0) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], t, a.freq, 16 * ks + 8 * hh, a.q_scale);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+  }
+
+
+  Flash<D> fl;
+  fl.init();
+
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 
@@ -201,16 +214,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
     return [=](int kr) { return kr <= tt && (kr >= lt || kr < se); };
   };
-  if (SPLIT && n_tiles <= 0) {  // no keys in this part of the walk: an empty partial
-    const int trow = t - a.row0;
-    if (t < r1 && hh == 0) {
-      const int64_t prow = ((int64_t)g * a.n_split + split) * ((int64_t)(a.row1 - a.row0) * G) +
-                           (int64_t)trow * G + hig;
-      a.part_ml[prow * 2 + 0] = 0.0f;
-      a.part_ml[prow * 2 + 1] = 0.0f;
-    }
-    return;
-  }
   flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb, load_k, load_v, full_of, vis_of);
 
   const float lsum = fl.total();
