@@ -543,8 +543,9 @@ struct SharedPlan {
   size_t off_tab = 0, off_k = 0, off_po = 0, off_pl = 0, off_tail = 0, total = 0;
 };
 
+// K-image tiles of block b: relative to the block (tile i = its tokens 64 i ..).
 int64_t tiles_of_block(const std::vector<int32_t>& off, int b) {
-  return cdiv(off[b + 1], kKeyTile) - off[b] / kKeyTile;
+  return cdiv(off[b + 1] - off[b], kKeyTile);
 }
 
 // Workspace layout (also the bound dbsa_workspace_bytes reports, with every

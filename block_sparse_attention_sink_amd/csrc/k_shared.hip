@@ -45,9 +45,11 @@ __device__ __forceinline__ SharedTab shared_tab(const int32_t* tab, const Shared
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// K tiles of the selected blocks, rotated at pool positions.  One workgroup
-// per (slot, KV head); slot s belongs to used block u (uslot[u] <= s <
-// uslot[u + 1]) and is its tile kt = off[b] / 64 + (s - uslot[u]).
+// K tiles of the selected blocks, rotated at pool positions.  Tiles are
+// relative to each block: tile i of block b holds its tokens off[b] + 64 i ..
+// + 63 (zero past the block), so only a block's last tile is partial.  One
+// workgroup per (slot, KV head); slot s belongs to used block u (uslot[u] <= s
+// < uslot[u + 1]) and is its tile i = s - uslot[u].
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void k_pack_shared_bf16(SharedPackArgs a) {
@@ -56,11 +58,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_shared_bf16(SharedPackAr
   const SharedTab tb = shared_tab(a.tab, a.t);
   const int slot = blockIdx.x, g = blockIdx.y;
   const int u = upper_index(tb.uslot, a.t.n_used, slot);
-  const int kt = tb.off[tb.ublk[u]] / kKeyTile + (slot - tb.uslot[u]);
+  const int b = tb.ublk[u];
   const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
-  const int64_t tok = (int64_t)kt * kKeyTile + key;
+  const int64_t tok = (int64_t)tb.off[b] + (int64_t)(slot - tb.uslot[u]) * kKeyTile + key;
   u32x4 k1 = u32x4{0u, 0u, 0u, 0u}, k2 = k1;
-  if (tok < a.n_tokens) {
+  if (tok < tb.off[b + 1]) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) +
                                                      (tok * a.hkv + g) * D);
     k1 = kp[c];
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_shared_bf16(SharedPackAr
 // ---------------------------------------------------------------------------
 // Shared-block attention.  Workgroup = 8 wavefronts x 32 packed rows of the
 // pairs (query, slot) that selected block b, chunk `chunk` of them; the
-// workgroup walks the 64-key tiles covering [off[b], off[b + 1]), the first
-// and last masked to the block.  Same LDS rings, loads and pipeline as
+// workgroup walks the block's 64-key tiles (tokens off[b] + 64 i ..), the
+// last one masked to the block.  Same LDS rings, loads and pipeline as
 // k_prefill_bf16.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -105,8 +107,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   const int key0 = __builtin_amdgcn_readfirstlane(tb.off[blk]);
   const int key1 = __builtin_amdgcn_readfirstlane(tb.off[blk + 1]);
   const int slot0 = __builtin_amdgcn_readfirstlane(tb.kslot[blk]);
-  const int kt0 = key0 / kKeyTile;
-  const int n_tiles = (key1 + kKeyTile - 1) / kKeyTile - kt0;
+  const int n_tiles = (key1 - key0 + kKeyTile - 1) / kKeyTile;
 
   // This lane's row: pair (batch row qb, slot of blk in its ids), token r,
   // head in group h.
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
     vo[jj] = (row * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8;
   }
   const int wsc = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t vtile = (int64_t)kKeyTile * a.hkv * D;
   auto load_k = [&](int it) {
     char* st = kring + (it % NS) * Gm::KBYTES;
     const u32x4* kt = kbase + (int64_t)it * Gm::TU4;
@@ -146,18 +146,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   };
   auto load_v = [&](int it) {
     char* st = vring + (it % NS) * Gm::VBYTES;
-    const int kt = kt0 + it;
-    if ((kt + 1) * kKeyTile <= a.n_tokens) {
-      const uint16_t* vt = vsrc + kt * vtile;
+    const int k0 = key0 + it * kKeyTile;
+    if (k0 + kKeyTile <= a.n_tokens) {  // (rows past the block are masked)
+      const uint16_t* vt = vsrc + (int64_t)k0 * a.hkv * D;
 #pragma unroll
       for (int jj = 0; jj < NPW; ++jj)
         dma16s(2u * vo[jj], vt, st + (wsc + jj * kPrefillWaves) * 1024);
-    } else {  // last tile of the pool: rows past it repeat its last key (masked)
+    } else {  // end of the pool: rows past it repeat its last key (masked)
 #pragma unroll
       for (int jj = 0; jj < NPW; ++jj) {
         const int o16 = (wave + jj * kPrefillWaves) * 1024 + lane * 16;
         const int row = o16 / Gm::ROW;
-        const int64_t tok = min(kt * kKeyTile + row, a.n_tokens - 1);
+        const int64_t tok = min(k0 + row, a.n_tokens - 1);
         dma16(vsrc + (tok * a.hkv + g) * D + Gm::v_phys(row, (o16 % Gm::ROW) >> 4) * 8,
               st + (wsc + jj * kPrefillWaves) * 1024);
       }
@@ -189,16 +189,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
 
-  // Every row sees the whole block: only the first and last tiles, which
-  // may reach into neighbouring blocks, need the element mask.
-  const auto full_of = [&](int it) {
-    const int k0 = (kt0 + it) * kKeyTile;
-    return k0 >= key0 && k0 + kKeyTile <= key1;
-  };
+  // Every row sees the whole block: only its last tile, which may reach
+  // past it, needs the element mask.
+  const auto full_of = [&](int it) { return key0 + (it + 1) * kKeyTile <= key1; };
   const auto vis_of = [&](int it) {
-    const int k0 = (kt0 + it) * kKeyTile;
-    const int lo = key0 - k0, hi = key1 - k0;
-    return [=](int kr) { return kr >= lo && kr < hi; };
+    const int hi = key1 - (key0 + it * kKeyTile);
+    return [=](int kr) { return kr < hi; };
   };
   flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb8, load_k, load_v, full_of, vis_of);
 
