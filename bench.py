@@ -44,8 +44,8 @@ KEY_TILE, WG_ROWS = 64, 256
 CSRC = os.path.join(ROOT, "block_sparse_attention_sink_amd", "csrc")
 PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("k_stage1.hip", "dbsa_device.hpp",
                                                    "dbsa_internal.hpp")]
-STAGE2_SOURCES = [os.path.join(CSRC, f) for f in ("k_stage2.hip", "dbsa_device.hpp",
-                                                  "dbsa_internal.hpp")]
+STAGE2_SOURCES = [os.path.join(CSRC, f) for f in ("k_shared.hip", "k_stage2.hip", "k_tables.hip",
+                                                  "dbsa_device.hpp", "dbsa_internal.hpp")]
 PREFILL_PROFILE = os.path.join(ROOT, "profiles", "k_prefill_bf16_stress_131072_sink_prev2.md")
 STAGE2_PROFILE = os.path.join(ROOT, "profiles", "stage2_llama31_pool_batch64x48.md")
 
