@@ -27,8 +27,11 @@ FLAGS = [
 # Kernel files only: scores and probabilities are never NaN (masked scores are
 # -inf, which stays honoured), so max/min need no NaN canonicalisation.  The
 # host file keeps full IEEE semantics for its argument checks.
-KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans"], "k_stage2.hip": ["-fno-honor-nans"],
-                "k_shared.hip": ["-fno-honor-nans"]}
+# The prefill's persistent item loop: machine-level loop-invariant code
+# motion would hoist constants and addresses out of it and keep them live
+# across the whole walk, which spills registers inside the walk.
+KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-licm"],
+                "k_stage2.hip": ["-fno-honor-nans"], "k_shared.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):

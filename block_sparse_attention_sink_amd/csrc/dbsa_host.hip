@@ -153,7 +153,7 @@ struct Stage1Plan {
   int32_t n_split = 1;       // key splits per query tile (short walks: appends)
   int32_t pack_log2 = 0;     // query heads of a KV head per workgroup (log2), bf16
   // workspace layout
-  size_t off_meta = 0, off_k = 0, off_po = 0, off_ml = 0, total = 0;
+  size_t off_meta = 0, off_k = 0, off_po = 0, off_ml = 0, off_queue = 0, total = 0;
   size_t meta_bytes = 0;
 };
 
@@ -197,6 +197,10 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
     const size_t tile = (size_t)kKeyTile * a->head_dim * 2;
     p.off_k = cur;
     cur = align_up(cur + (size_t)a->n_kv_heads * p.n_slots * tile);
+  }
+  if (a->dtype == DBSA_BF16 && p.n_split == 1) {
+    p.off_queue = cur;
+    cur = align_up(cur + kPrefillQueueWords * sizeof(uint32_t));
   }
   if (p.n_split > 1) {
     const size_t prow = (size_t)p.n_split * (p.row1 - p.row0) * a->n_q_heads;
@@ -246,6 +250,17 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
   pa.n_split = p.n_split;
   pa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(w + p.off_po) : nullptr;
   pa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(w + p.off_ml) : nullptr;
+  pa.queue = (a->dtype == DBSA_BF16 && p.n_split == 1) ? reinterpret_cast<uint32_t*>(w + p.off_queue)
+                                                        : nullptr;
+  pa.n_workers = 0;
+  if (pa.queue != nullptr) {
+    // One persistent workgroup per compute unit (a workgroup fills one).
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "compute unit count");
+    pa.n_workers = std::max(n_cu, 1);
+  }
   if (a->dtype == DBSA_BF16) {
     PackArgs ka;
     ka.k = k;
@@ -257,6 +272,7 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
     ka.win_tile1 = p.win_tile1;
     ka.n_slots = p.n_slots;
     ka.freq = freq;
+    ka.queue = pa.queue;
     hipError_t e = launch_pack(ka, a->head_dim, a->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "launch k_pack");
     pa.k_tiles = ka.k_tiles;

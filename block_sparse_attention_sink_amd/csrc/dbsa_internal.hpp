@@ -18,6 +18,7 @@ constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (2 per SIMD)
 constexpr int kPrefillRows = kRowsPerWave * kPrefillWaves;  // 256 query rows per workgroup
 constexpr int kPrefillStages = 4;  // LDS stages per K ring and per V ring
 constexpr int kPrefillPackHeads = 4;  // most query heads of one KV head per prefill workgroup
+constexpr int kPrefillQueueWords = 8;  // prefill work counters, one per XCD
 constexpr int kMaxSegments = 1024;  // context segments per batch row in Stage 2
 constexpr int kQueryLoaders = 4;   // Stage-2 wavefronts that load and rotate the tiles
 constexpr int kQueryLead = 3;      // tiles each of their threads keeps in flight
@@ -44,6 +45,7 @@ struct PackArgs {
   int32_t win_tile1;
   int32_t n_slots;      // sink_tiles + (win_tile1 - win_tile0)
   RopeFreq freq;
+  uint32_t* queue;      // non-null: the prefill's 8 work counters, zeroed here
 };
 
 // Small per-call int32 tables travel in the kernel arguments (kInlineInts
@@ -86,6 +88,11 @@ struct PrefillArgs {
   int32_t n_split;
   float* part_o;
   float* part_ml;
+  // Whole walks (n_split == 1): a persistent grid of n_workers workgroups
+  // takes the items from 8 counters (kPrefillQueueWords), zeroed by the pack
+  // kernel of the same call.
+  uint32_t* queue;
+  int32_t n_workers;
   int32_t n_inline;         // > 0: the offsets are `inl` below
   int32_t inl[kInlineInts];
 };

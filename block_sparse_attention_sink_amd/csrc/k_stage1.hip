@@ -28,6 +28,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
   constexpr int CP = D / 16;  // chunk pairs per key row (first half / second half)
   constexpr int CR = D / 8;   // 16-byte chunks per key row
   const int slot = blockIdx.x, g = blockIdx.y;
+  if (a.queue != nullptr && slot == 0 && g == 0 && threadIdx.x < 8) a.queue[threadIdx.x] = 0u;
   const int kt = slot < a.sink_tiles ? slot : a.win_tile0 + (slot - a.sink_tiles);
   const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
   const int64_t tok = (int64_t)kt * kKeyTile + key;
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   char* const kring = lds;
   char* const vring = lds + NS * Gm::KBYTES;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hh = lane >> 5, col = lane & 31;
+  __shared__ int s_next[2];  // items of the next two rounds (written by thread 0)
+  const int tid = threadIdx.x;
 
   // Logical work item: (kv head g, query tile qt, key split, group of P =
   // 2^pack_log2 query heads of g).  The workgroup's 256 rows are 256 / P
@@ -75,8 +76,43 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int pl = a.pack_log2, P = 1 << pl;
   const int HS = G >> pl;  // head groups per KV head
   const int nsp = SPLIT ? a.n_split : 1;
-  const int lam = xcd_logical(blockIdx.x, gridDim.x);
   const int per_g = a.n_qtiles * nsp * HS;
+
+  // Without SPLIT the grid is persistent (about one workgroup per compute
+  // unit) and takes items from a queue: the items are cut into 8 consecutive
+  // ranges, one per XCD (neighbouring query tiles of one KV head share K/V in
+  // that XCD's L2), each with a counter in a.queue that the pack kernel
+  // zeroed.  A workgroup takes the next item of its own XCD's range and,
+  // once that is used up, of the other ranges in turn, so XCDs that run
+  // faster (their clocks differ) finish the work of slower ones and no
+  // compute unit waits for the hardware dispatcher between items.
+  const int n_items = per_g * a.hkv;
+  const int qq = n_items >> 3, qr = n_items & 7;
+  const auto claim = [&]() -> int {  // (one thread)
+    const int x0 = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // XCC_ID
+    for (int d = 0; d < 8; ++d) {
+      const int x = (x0 + d) & 7;
+      const int size = qq + (x < qr ? 1 : 0);
+      if (size == 0) continue;
+      const int i = (int)atomicAdd(a.queue + x, 1u);
+      if (i < size) return (x < qr ? x * (qq + 1) : qr * (qq + 1) + (x - qr) * qq) + i;
+    }
+    return -1;
+  };
+
+  // One work item (round k); thread 0 leaves the item it claims for the
+  // next round in s_next[(k + 1) & 1].
+  const auto run = [&](const int lam, const int k) {
+  // (The lane index and the argument block pass through empty asm
+  // statements so that nothing derived from them is hoisted out of the item
+  // loop: kept live across items, those values would not fit the registers.)
+  int tix = tid;
+  asm volatile("" : "+v"(tix));
+  auto kargs = (const __attribute__((address_space(4))) PrefillArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kargs));
+  const auto& a = *kargs;
+  const int wave = tix >> 6, lane = tix & 63;
+  const int hh = lane >> 5, col = lane & 31;
   const int g = lam / per_g;
   const int rem = lam - g * per_g;
   const int qt = rem / (nsp * HS);
@@ -91,19 +127,59 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int wrow = (wave >> pl) * kRowsPerWave;  // this wave's first token, from r0
   const int t = r0 + wrow + col;
 
+  // Q first: its address needs only the row and the head, so its latency
+  // overlaps the block lookups and the first tile requests below.
+  u32x4 raw[KS];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)(min(t, r1 - 1) - a.q_row0) * a.hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = qp[2 * ks + hh];
+  }
+
   // Visible key intervals [Notes, Method > Stage 1, item 2]:
   // row t sees [lo(t), t] with lo(t) = start of block max(blk(t) - j, 0),
   // plus the anchor block [0, sink_end) when the sink is on.
-  const int32_t* off = a.n_inline ? kernarg_ints(offsetof(PrefillArgs, inl)) : a.offsets;
   const int nb = a.n_blocks;
-  // (The table may sit in the kernel arguments or in device memory, so the
-  // compiler cannot tell that the workgroup-wide values below are uniform:
-  // say so, which keeps them, and the tile addresses built from them, in
-  // scalar registers.)
-  const int sink_end = __builtin_amdgcn_readfirstlane(a.sink ? off[1] : 0);
-  const int lo_t = off[max(upper_index(off, nb, min(t, r1 - 1)) - a.j, 0)];
-  const int lo_first = __builtin_amdgcn_readfirstlane(off[max(upper_index(off, nb, r0) - a.j, 0)]);
-  const int lo_last = __builtin_amdgcn_readfirstlane(off[max(upper_index(off, nb, r1 - 1) - a.j, 0)]);
+  // blk(x) = number of block starts off[1 .. nb - 1] at or before x.  The
+  // rows of the workgroup lie in blocks b_first = blk(r0) .. b_last =
+  // blk(r1 - 1), usually one or two.  With the table in the kernel arguments
+  // (at most 511 blocks) every lane compares 8 entries and ballots count
+  // them, and the other reads are scalar loads that wait for nothing else;
+  // a table in device memory is searched.  (Readfirstlane tells the compiler
+  // that these values are workgroup-uniform, which keeps them, and the tile
+  // addresses built from them, in scalar registers.)
+  int sink_end, lo_first, lo_last, lo_t;
+  const auto lookup = [&](auto off, int b_first, int b_last) {
+    b_first = __builtin_amdgcn_readfirstlane(b_first);
+    b_last = __builtin_amdgcn_readfirstlane(b_last);
+    sink_end = __builtin_amdgcn_readfirstlane(a.sink ? off[1] : 0);
+    lo_first = __builtin_amdgcn_readfirstlane(off[max(b_first - a.j, 0)]);
+    lo_last = __builtin_amdgcn_readfirstlane(off[max(b_last - a.j, 0)]);
+    lo_t = lo_first;
+    for (int bb = b_first + 1; bb <= b_last; ++bb)
+      if (__builtin_amdgcn_readfirstlane(off[bb]) <= t)
+        lo_t = __builtin_amdgcn_readfirstlane(off[max(bb - a.j, 0)]);
+  };
+  if (a.n_inline) {
+    const auto off = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
+        offsetof(PrefillArgs, inl));
+    int e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = off[8 * lane + k];
+    int c0 = 0, c1 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = 8 * lane + k;
+      const bool in = idx >= 1 && idx < nb;
+      c0 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(in && e[k] <= r0));
+      c1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(in && e[k] <= r1 - 1));
+    }
+    lookup(off, c0, c1);
+  } else {
+    lookup(a.offsets, upper_index(a.offsets, nb, r0), upper_index(a.offsets, nb, r1 - 1));
+  }
   const int win0 = lo_first / kKeyTile;
   const int win1 = (r1 + kKeyTile - 1) / kKeyTile;
   int nsink = 0;
@@ -179,24 +255,44 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     }
     return;
   }
+  // Q has landed (the table lookups waited for it, or had the time to): the
+  // compiler, which does not count the tile requests, then places no wait
+  // for Q after them.
+  waitcnt<0, 15>();
   flash_walk_start(n_tiles, load_k, load_v);
+  if constexpr (!SPLIT)
+    if (tid == 0) s_next[(k + 1) & 1] = claim();  // (its latency hides behind the walk)
 
   // Q: rotate at position t, fold scale * log2(e), round once to bf16.
   bf16x8 qb[KS];
   {
-    u32x4 raw[KS];
-    const bool live = t < r1;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)(t - a.q_row0) * a.hq + head) * D);
+    if (t >= r1) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < KS; ++ks) raw[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // (The two lane halves' frequencies are read as scalars and selected:
+    // a per-lane index would make them vector loads queued behind the tile
+    // requests above.  Their address passes through an empty asm statement
+    // so the loads stay here instead of being hoisted out of the item loop,
+    // where they would be live across it.)
+    auto frev = reinterpret_cast<const __attribute__((address_space(4))) double*>(
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
+        offsetof(PrefillArgs, freq) + offsetof(RopeFreq, rev));
+    asm volatile("" : "+s"(frev));
 #pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], t, a.freq, 16 * ks + 8 * hh, a.q_scale);
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      float c[8], sn[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        double f0 = frev[16 * ks + r], f1 = frev[16 * ks + 8 + r];
+        asm volatile("" : "+s"(f0), "+s"(f1));  // (kept as two scalar loads)
+        rope_cs(t, hh ? f1 : f0, c[r], sn[r]);
+      }
+      rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
-
 
   Flash<D> fl;
   fl.init();
@@ -262,6 +358,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     if (trow < r1)
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) +
                                 ((int64_t)(trow - a.q_row0) * a.hq + head) * D + ch * 8) = v;
+  }
+  };
+
+  if constexpr (SPLIT) {
+    run(xcd_logical(blockIdx.x, gridDim.x), 0);
+  } else {
+    if (tid == 0) s_next[0] = claim();
+    __syncthreads();
+    for (int k = 0;; ++k) {
+      const int item = s_next[k & 1];
+      if (item < 0) break;
+      run(item, k);
+      // The next item, and (every wave has finished with the K ring, which
+      // held the output staging) free LDS for its first tile requests.
+      __syncthreads();
+    }
   }
 }
 
@@ -364,7 +476,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStre
       hipLaunchKernelGGL(k_rows_f32<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid(a.n_qtiles * (a.hq >> a.pack_log2) * a.n_split);
+  const int items = a.n_qtiles * (a.hq >> a.pack_log2) * a.n_split;
+  const dim3 grid(a.n_split > 1 ? items : std::min(items, a.n_workers));
   const dim3 block(64 * kPrefillWaves);
   if (a.n_split > 1) {
     if (head_dim == 128) hipLaunchKernelGGL((k_prefill_bf16<128, true>), grid, block, 0, stream, a);
