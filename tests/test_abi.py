@@ -14,7 +14,12 @@ from block_sparse_attention_sink_amd import dbsa
 from block_sparse_attention_sink_amd.inputs import llama31_inv_freq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FAKE = 0x100000  # aligned, never dereferenced: every case below fails validation first
+# Aligned, never dereferenced: every call below fails a check before anything
+# is enqueued.  A call that must pass the argument checks gets a workspace too
+# small to hold it, so that it stops at the workspace check (the last one, and
+# still before any launch): on a GPU machine a launch would read and write
+# these fake addresses.
+FAKE = 0x100000
 
 
 @pytest.fixture(scope="module")
@@ -101,9 +106,9 @@ def test_prefill_layers_validation(lib):
     a = _attn()
     q_ext, kv_ext = 21 * 4 * 128, 21 * 2 * 128
 
-    def call(n, qs, kvs, os_):
+    def call(n, qs, kvs, os_, ws_bytes=1 << 40):
         return lib.dbsa_prefill_layers(ctypes.byref(a), ctypes.byref(blocks.t), n, FAKE, qs, FAKE,
-                                       FAKE, kvs, FAKE, os_, FAKE, 1 << 40, None)
+                                       FAKE, kvs, FAKE, os_, FAKE, ws_bytes, None)
     assert call(0, q_ext, kv_ext, q_ext) == dbsa.EINVAL
     assert "n_layers" in _err(lib)
     assert call(2, q_ext, kv_ext, q_ext - 8) == dbsa.EINVAL  # outputs would overlap
@@ -111,17 +116,19 @@ def test_prefill_layers_validation(lib):
     assert call(2, q_ext, kv_ext // 2, q_ext) == dbsa.EINVAL
     assert call(2, q_ext + 4, kv_ext, q_ext) == dbsa.EINVAL  # 8 bytes: misaligned layers
     assert "16 bytes" in _err(lib)
-    # shared inputs (stride 0) and a single layer with any stride pass the checks
-    assert call(3, 0, 0, q_ext) not in (dbsa.EINVAL, dbsa.EUNSUPPORTED)
-    assert call(1, 3, 5, 7) not in (dbsa.EINVAL, dbsa.EUNSUPPORTED)
+    # shared inputs (stride 0) and a single layer with any stride pass the
+    # argument checks (and stop at the workspace check)
+    assert call(3, 0, 0, q_ext, ws_bytes=16) == dbsa.ENOSPC and "workspace" in _err(lib)
+    assert call(1, 3, 5, 7, ws_bytes=16) == dbsa.ENOSPC and "workspace" in _err(lib)
 
 
 def test_rope_table_validation(lib):
     ok_blocks = dbsa.Blocks([5, 7, 9], 1, 2)
     table = llama31_inv_freq(5e5, 128)
-    # a valid table passes the argument checks (the launch itself needs a GPU)
-    assert _prefill(lib, dbsa.attn_t(4, 2, 128, dbsa.BF16, table), ok_blocks) not in (
-        dbsa.EINVAL, dbsa.EUNSUPPORTED)
+    # a valid table passes the argument checks (and stops at the workspace check)
+    assert _prefill(lib, dbsa.attn_t(4, 2, 128, dbsa.BF16, table), ok_blocks,
+                    ws_bytes=16) == dbsa.ENOSPC
+    assert "workspace" in _err(lib)
     for bad in (np.nan, -1.0, np.inf):
         t = table.copy()
         t[7] = bad
@@ -223,7 +230,8 @@ def test_workspace_sizes(lib):
     assert q > 0
 
 
-def _span_call(lib, fn, src, ln, pool=100, cap=1 << 20, n_new=4, tail_cap=1 << 20):
+def _span_call(lib, fn, src, ln, pool=100, cap=1 << 20, n_new=4, tail_cap=1 << 20,
+               ws_bytes=1 << 40):
     src = np.ascontiguousarray(np.atleast_2d(np.asarray(src, np.int32)))
     ln = np.ascontiguousarray(np.atleast_2d(np.asarray(ln, np.int32)))
     p32 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -234,11 +242,11 @@ def _span_call(lib, fn, src, ln, pool=100, cap=1 << 20, n_new=4, tail_cap=1 << 2
         return lib.dbsa_gather_rope_spans(ctypes.byref(a), p32(src), p32(ln), n, batch, pool,
                                           FAKE, FAKE, FAKE, FAKE, cap,
                                           out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                          FAKE, 1 << 40, None)
+                                          FAKE, ws_bytes, None)
     return lib.dbsa_query_attn_spans(ctypes.byref(a), p32(src), p32(ln), n, batch, pool, FAKE,
                                      FAKE, n_new, FAKE, FAKE, FAKE, FAKE, FAKE,
                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), tail_cap,
-                                     FAKE, FAKE, 1 << 40, None)
+                                     FAKE, FAKE, ws_bytes, None)
 
 
 @pytest.mark.parametrize("fn", ["gather", "query"])
@@ -270,9 +278,12 @@ def test_span_validation(lib, fn):
         assert _span_call(lib, fn, [gaps], [np.ones(n, np.int32)], pool=4 * n) == \
             dbsa.EUNSUPPORTED
         assert "exceed" in _err(lib)
+        # (A workspace too small to hold the call stops it after the span
+        # checks, before anything is enqueued on the fake pointers.)
         adj = np.arange(n, dtype=np.int32)
-        assert _span_call(lib, fn, [adj], [np.ones(n, np.int32)], pool=4 * n) not in (
-            dbsa.EINVAL, dbsa.EUNSUPPORTED)
+        assert _span_call(lib, fn, [adj], [np.ones(n, np.int32)], pool=4 * n,
+                          ws_bytes=16) == dbsa.ENOSPC
+        assert "workspace" in _err(lib)
 
 
 def test_noalloc_entry_checks_before_any_hip_call(lib):
