@@ -27,11 +27,12 @@ FLAGS = [
 # Kernel files only: scores and probabilities are never NaN (masked scores are
 # -inf, which stays honoured), so max/min need no NaN canonicalisation.  The
 # host file keeps full IEEE semantics for its argument checks.
-# The prefill's persistent item loop: machine-level loop-invariant code
-# motion would hoist constants and addresses out of it and keep them live
-# across the whole walk, which spills registers inside the walk.
+# The persistent item loops (prefill, shared-block Stage 2): machine-level
+# loop-invariant code motion would hoist constants and addresses out of them
+# and keep them live across the whole walk, which spills registers inside it.
 KERNEL_FLAGS = {"k_stage1.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-licm"],
-                "k_stage2.hip": ["-fno-honor-nans"], "k_shared.hip": ["-fno-honor-nans"]}
+                "k_stage2.hip": ["-fno-honor-nans"],
+                "k_shared.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-licm"]}
 
 
 def _run(cmd):

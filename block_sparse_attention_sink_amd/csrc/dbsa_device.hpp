@@ -116,6 +116,53 @@ __device__ __forceinline__ void rope_rotate_chunk(u32x4& x1, u32x4& x2, int64_t 
 }
 
 
+// RoPE angles of a workgroup's query rows through an LDS table: the rows of a
+// 256-row workgroup hold only a few distinct positions (the G heads of a token
+// share one), so each (position, frequency) cos / sin is computed once, by one
+// thread, instead of once per row.  Table row j (position pos_of(j)) holds
+// the D / 2 (cos, sin) pairs, padded by 16 bytes against bank conflicts.
+template <int D>
+struct AngleTable {
+  static constexpr int H = D / 2;
+  static constexpr int ROWB = H * 8 + 16;  // bytes per position
+  // Fill rows 0 .. n_pos - 1 (all threads of the workgroup call this, in
+  // whole wavefronts; the caller then synchronises the workgroup).  Entry e
+  // is position e % n_pos, frequencies 8 (e / n_pos) .. + 7: with n_pos a
+  // multiple of 64 the frequencies are the same across a wavefront, and are
+  // read as scalars.
+  template <typename PosOf, typename Freq>
+  static __device__ __forceinline__ void fill(char* tab, int n_pos, int tid, int n_threads,
+                                              PosOf&& pos_of, Freq&& freq) {
+    for (int e = tid; e < n_pos * (H / 8); e += n_threads) {
+      const int j = e % n_pos;
+      int f0 = (e / n_pos) * 8;
+      if (n_pos % 64 == 0) f0 = __builtin_amdgcn_readfirstlane(f0);
+      const int64_t p = pos_of(j);
+      f32x4* dst = reinterpret_cast<f32x4*>(tab + j * ROWB + f0 * 8);
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        float c0, s0, c1, s1;
+        rope_cs(p, freq(f0 + i), c0, s0);
+        rope_cs(p, freq(f0 + i + 1), c1, s1);
+        dst[i / 2] = f32x4{c0, s0, c1, s1};
+      }
+    }
+  }
+  // cos / sin of frequencies f0 .. f0 + 7 at table row j.
+  static __device__ __forceinline__ void read8(const char* tab, int j, int f0, float (&c)[8],
+                                               float (&s)[8]) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(tab + j * ROWB + f0 * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 w = src[i];
+      c[2 * i] = w[0];
+      s[2 * i] = w[1];
+      c[2 * i + 1] = w[2];
+      s[2 * i + 1] = w[3];
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tile layouts (one 64-key tile of one KV head), both [64 keys][D] bf16:
 //   K tile  rotated keys; read as the A operand of S^T = K Q^T (16 bytes/lane).
@@ -627,6 +674,47 @@ __device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char
   wait_vm(0);
   barrier_nofence();
   fl.pv(vs((n_tiles - 1) % kPrefillStages), vbase, pr);
+}
+
+// Work queue of a persistent grid (about one workgroup per compute unit):
+// items [0, n) are cut into 8 consecutive ranges, one per XCD (neighbouring
+// items share K/V in that XCD's L2), each with a counter in `queue` that the
+// kernel launched before zeroed.  A workgroup takes the next item of its own
+// XCD's range and, once that is used up, of the other ranges in turn, so XCDs
+// that run faster (their clocks differ) finish the work of slower ones, and no
+// compute unit waits on the hardware dispatcher between items.  Called by one
+// thread; -1 when every range is used up.
+__device__ __forceinline__ int queue_claim(uint32_t* queue, int n) {
+  const int qq = n >> 3, qr = n & 7;
+  const int x0 = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // XCC_ID
+  for (int d = 0; d < 8; ++d) {
+    const int x = (x0 + d) & 7;
+    const int size = qq + (x < qr ? 1 : 0);
+    if (size == 0) continue;
+    const int i = (int)atomicAdd(queue + x, 1u);
+    if (i < size) return (x < qr ? x * (qq + 1) : qr * (qq + 1) + (x - qr) * qq) + i;
+  }
+  return -1;
+}
+
+// The item loop of a persistent grid: run(item, k) handles round k's item;
+// its thread 0 stores the item of round k + 1 in s_next[(k + 1) & 1] (claimed
+// early, so the claim's latency hides behind the round).  Every wave reads
+// s_next[k & 1] before the round's barriers, so the round-(k + 1) slot is
+// free when thread 0 writes it; the barrier after each round also frees the
+// LDS for the next round's first tile requests.  (Callers build with machine
+// loop-invariant code motion off: hoisted out of this loop, constants and
+// addresses would stay live across the whole walk and spill registers.)
+template <typename Run>
+__device__ __forceinline__ void queue_loop(uint32_t* queue, int n, int* s_next, Run&& run) {
+  if (threadIdx.x == 0) s_next[0] = queue_claim(queue, n);
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const int item = s_next[k & 1];
+    if (item < 0) break;
+    run(item, k);
+    __syncthreads();
+  }
 }
 
 // Workgroup order: the hardware hands consecutive workgroup ids to the 8 XCDs

@@ -212,6 +212,17 @@ void stage1_layout(const dbsa_attn_t* a, Stage1Plan& p, bool whole_pool, int sin
   p.total = cur;
 }
 
+// Workgroups of a persistent grid: one per compute unit of the current
+// device (each fills one).
+int compute_units(int32_t* n) {
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "compute unit count");
+  *n = std::max(n_cu, 1);
+  return DBSA_OK;
+}
+
 int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Plan& p,
                   const void* q, int32_t q_row0, const void* k, const void* v, void* o,
                   void* ws, hipStream_t s, bool upload_table = true) {
@@ -254,12 +265,8 @@ int launch_stage1(const dbsa_attn_t* a, const dbsa_blocks_t* blk, const Stage1Pl
                                                         : nullptr;
   pa.n_workers = 0;
   if (pa.queue != nullptr) {
-    // One persistent workgroup per compute unit (a workgroup fills one).
-    int dev = 0, n_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "compute unit count");
-    pa.n_workers = std::max(n_cu, 1);
+    const int rc = compute_units(&pa.n_workers);
+    if (rc) return rc;
   }
   if (a->dtype == DBSA_BF16) {
     PackArgs ka;
@@ -556,7 +563,7 @@ struct SharedPlan {
   int32_t rq = 0, n_pairs = 0;
   SegPlan sp;                 // tail / new-token pass
   QueryPlan qp;
-  size_t off_tab = 0, off_k = 0, off_po = 0, off_pl = 0, off_tail = 0, total = 0;
+  size_t off_tab = 0, off_k = 0, off_po = 0, off_pl = 0, off_queue = 0, off_tail = 0, total = 0;
 };
 
 // K-image tiles of block b: relative to the block (tile i = its tokens 64 i ..).
@@ -577,6 +584,8 @@ void shared_layout(const dbsa_attn_t* a, int32_t batch, int32_t n_ids, SharedPla
   cur = align_up(cur + prow * d * 2);
   p.off_pl = cur;
   cur = align_up(cur + prow * sizeof(float));
+  p.off_queue = cur;
+  cur = align_up(cur + kPrefillQueueWords * sizeof(uint32_t));
   p.off_tail = cur;
   p.total = cur + p.qp.total;
 }
@@ -702,6 +711,7 @@ int launch_shared_path(const dbsa_attn_t* a, int32_t batch, int32_t n_ids, int32
     pk.n_tokens = n_tokens;
     pk.hkv = a->n_kv_heads;
     pk.freq = freq;
+    pk.queue = reinterpret_cast<uint32_t*>(w + p.off_queue);
     e = launch_shared_pack(pk, a->head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "launch shared pack");
     SharedArgs sa;
@@ -720,6 +730,9 @@ int launch_shared_path(const dbsa_attn_t* a, int32_t batch, int32_t n_ids, int32
     sa.rq = p.rq;
     sa.q_scale = q_scale_of(a);
     sa.freq = freq;
+    sa.queue = pk.queue;
+    rc = compute_units(&sa.n_workers);
+    if (rc) return rc;
     e = launch_shared(sa, a->head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "launch shared");
   }

@@ -207,6 +207,7 @@ struct SharedPackArgs {
   SharedTables t;
   int32_t n_tokens, hkv;
   RopeFreq freq;
+  uint32_t* queue;          // k_shared_bf16's kPrefillQueueWords work counters, zeroed here
 };
 
 struct SharedArgs {
@@ -221,6 +222,8 @@ struct SharedArgs {
   int32_t rq;               // rows per (batch row, kv head) = n_new * (hq / hkv)
   float q_scale;            // softmax scale * log2(e)
   RopeFreq freq;
+  uint32_t* queue;          // work counters (see queue_claim)
+  int32_t n_workers;        // persistent workgroups (compute units)
 };
 
 struct MergeArgs {

@@ -20,7 +20,8 @@
 //                        head in GQA group) over one block's tiles: the
 //                        software-pipelined core of the prefill on
 //                        v_mfma_f32_32x32x16_bf16; writes O / l (bf16) and
-//                        m + log2 l per row.
+//                        m + log2 l per row.  A persistent grid that takes
+//                        its items from a work queue (zeroed by the pack).
 #include "dbsa_device.hpp"
 
 namespace dbsa {
@@ -37,7 +38,8 @@ struct SharedTab {
   const int32_t* uslot;
 };
 
-__device__ __forceinline__ SharedTab shared_tab(const int32_t* tab, const SharedTables& t) {
+template <typename Tables>  // (SharedTables, in any address space)
+__device__ __forceinline__ SharedTab shared_tab(const int32_t* tab, const Tables& t) {
   return SharedTab{tab + t.o_off,   tab + t.o_bstart, tab + t.o_istart, tab + t.o_pairs,
                    tab + t.o_kslot, tab + t.o_ublk,   tab + t.o_uslot};
 }
@@ -57,6 +59,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_shared_bf16(SharedPackAr
   constexpr int CP = D / 16, CR = D / 8;
   const SharedTab tb = shared_tab(a.tab, a.t);
   const int slot = blockIdx.x, g = blockIdx.y;
+  if (slot == 0 && g == 0 && threadIdx.x < kPrefillQueueWords) a.queue[threadIdx.x] = 0u;
   const int u = upper_index(tb.uslot, a.t.n_used, slot);
   const int b = tb.ublk[u];
   const int tid = threadIdx.x, key = tid / CP, c = tid % CP;
@@ -91,16 +94,39 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   char* const kring = lds;
   char* const vring = lds + NS * Gm::KBYTES;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ int s_next[2];
+  const int n_all = a.t.n_items * a.hkv;
+
+  // Work item lam = (kv head g, item); items are ordered by block, so each
+  // XCD's range of the work queue walks consecutive chunks of one block (its
+  // K/V tiles stay in that L2).  Round k of the persistent loop.
+  const auto run = [&](const int lam, const int k) {
+  // (The lane index and the argument block pass through empty asm
+  // statements so that nothing derived from them is hoisted out of the item
+  // loop: kept live across items, those values would not fit the registers.)
+  int tix = threadIdx.x;
+  asm volatile("" : "+v"(tix));
+  auto kargs = (const __attribute__((address_space(4))) SharedArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kargs));
+  const auto& a = *kargs;
+  const int tid = tix, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, col = lane & 31;
   const SharedTab tb = shared_tab(a.tab, a.t);
-
-  // Work item: (kv head g, item); items are ordered by block, so each XCD
-  // walks consecutive chunks of one block (its K/V tiles stay in that L2).
-  const int lam = xcd_logical(blockIdx.x, gridDim.x);
   const int g = lam / a.t.n_items;
   const int item = lam - g * a.t.n_items;
-  const int blk = __builtin_amdgcn_readfirstlane(upper_index(tb.istart, a.t.n_blocks, item));
+  // The item's block: istart is ascending from istart[0] = 0, so blk = the
+  // number of b in [1, n_blocks) with istart[b] <= item, counted 128 entries
+  // at a time with ballots (one load latency for up to 128 blocks, instead of
+  // a chain of dependent loads).
+  int blk = 0;
+  for (int b0 = 0; b0 < a.t.n_blocks; b0 += 128) {
+    const int ba = b0 + lane, bb = b0 + 64 + lane;
+    const int ia = ba < a.t.n_blocks ? tb.istart[ba] : INT32_MAX;
+    const int ib = bb < a.t.n_blocks ? tb.istart[bb] : INT32_MAX;
+    blk += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ba >= 1 && ia <= item)) +
+           __builtin_popcountll(__builtin_amdgcn_ballot_w64(ib <= item));
+  }
+  blk = __builtin_amdgcn_readfirstlane(blk);
   const int chunk = item - __builtin_amdgcn_readfirstlane(tb.istart[blk]);
   const int p0 = __builtin_amdgcn_readfirstlane(tb.bstart[blk]);
   const int n_rows = (__builtin_amdgcn_readfirstlane(tb.bstart[blk + 1]) - p0) * a.rq;
@@ -110,15 +136,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
   const int n_tiles = (key1 - key0 + kKeyTile - 1) / kKeyTile;
 
   // This lane's row: pair (batch row qb, slot of blk in its ids), token r,
-  // head in group h.
+  // head in group h (the pair itself is read after the first tile requests).
   const int G = a.hq / a.hkv;
   const int rho = chunk * kPrefillRows + wave * kRowsPerWave + col;
   const bool live = rho < n_rows;
   const int pr = live ? rho / a.rq : 0;
   const int rr = live ? rho - pr * a.rq : 0;
-  const int qi = tb.pairs[2 * (p0 + pr)];
-  const int shift = tb.pairs[2 * (p0 + pr) + 1];
-  const int qb = qi >> 16, qslot = qi & 0xffff;
   const int r = rr / G;
   const int head = g * G + (rr - r * G);
 
@@ -164,6 +187,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
     }
   };
   flash_walk_start(n_tiles, load_k, load_v);
+  if (tid == 0) s_next[(k + 1) & 1] = queue_claim(a.queue, n_all);
+  const int qi = tb.pairs[2 * (p0 + pr)];
+  const int shift = tb.pairs[2 * (p0 + pr) + 1];
+  const int qb = qi >> 16, qslot = qi & 0xffff;
 
   // Q of the row, rotated at its position relative to the block's pool
   // placement, scale * log2(e) folded in, rounded once to bf16.
@@ -174,14 +201,49 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
         static_cast<const uint16_t*>(a.q) + (((int64_t)qb * a.n_new + r) * a.hq + head) * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) raw[ks] = live ? qp[2 * ks + hh] : u32x4{0u, 0u, 0u, 0u};
+    auto frev = reinterpret_cast<const __attribute__((address_space(4))) double*>(
+        (const __attribute__((address_space(4))) char*)kargs + offsetof(SharedArgs, freq) +
+        offsetof(RopeFreq, rev));
+    using AT = AngleTable<D>;
+    // The G rows of one (pair, token) share a position: with G >= 4 the
+    // workgroup's 256 / G positions go through an LDS table in V stages 1-3
+    // (untouched until the walk's first requests), one cos / sin per
+    // (position, frequency).  Uniform condition.
+    if (G >= 4 && (kPrefillRows / G) * AT::ROWB <= 3 * Gm::VBYTES) {
+      char* const tab = vring + Gm::VBYTES;
+      AT::fill(tab, kPrefillRows / G, tid, 64 * kPrefillWaves,
+               [&](int j) -> int64_t {
+                 const int rj = chunk * kPrefillRows + j * G;  // first row of position j
+                 if (rj >= n_rows) return 0;
+                 const int prj = rj / a.rq;
+                 return (int64_t)tb.pairs[2 * (p0 + prj) + 1] + (rj - prj * a.rq) / G;
+               },
+               [&](int f) { return (double)frev[f]; });
+      __syncthreads();
+      const int jl = (wave * kRowsPerWave + col) / G;
 #pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-      rope_rotate_chunk(raw[ks], raw[ks + KS / 2], (int64_t)shift + r, a.freq, 16 * ks + 8 * hh,
-                        a.q_scale);
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        float c[8], sn[8];
+        AT::read8(tab, jl, 16 * ks + 8 * hh, c, sn);
+        rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
+      }
+    } else {
+      // (The two lane halves' frequencies are scalar loads, selected per lane.)
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        float c[8], sn[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double f0 = frev[16 * ks + i], f1 = frev[16 * ks + 8 + i];
+          asm volatile("" : "+s"(f0), "+s"(f1));  // (kept as two scalar loads)
+          rope_cs((int64_t)shift + r, hh ? f1 : f0, c[i], sn[i]);
+        }
+        rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb8[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
-
 
   Flash<D> fl;
   fl.init();
@@ -231,6 +293,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
       *reinterpret_cast<u32x4*>(a.part_o + row * D + ch * 8) = v;
     }
   }
+  };
+  queue_loop(a.queue, n_all, s_next, run);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,7 +310,7 @@ hipError_t launch_shared_pack(const SharedPackArgs& a, int head_dim, hipStream_t
 }
 
 hipError_t launch_shared(const SharedArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid(a.t.n_items * a.hkv);
+  const dim3 grid(std::min(a.t.n_items * a.hkv, a.n_workers));
   if (head_dim == 128)
     hipLaunchKernelGGL(k_shared_bf16<128>, grid, dim3(64 * kPrefillWaves), 0, stream, a);
   else

@@ -78,27 +78,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   const int nsp = SPLIT ? a.n_split : 1;
   const int per_g = a.n_qtiles * nsp * HS;
 
-  // Without SPLIT the grid is persistent (about one workgroup per compute
-  // unit) and takes items from a queue: the items are cut into 8 consecutive
-  // ranges, one per XCD (neighbouring query tiles of one KV head share K/V in
-  // that XCD's L2), each with a counter in a.queue that the pack kernel
-  // zeroed.  A workgroup takes the next item of its own XCD's range and,
-  // once that is used up, of the other ranges in turn, so XCDs that run
-  // faster (their clocks differ) finish the work of slower ones and no
-  // compute unit waits for the hardware dispatcher between items.
+  // Without SPLIT the grid is persistent and takes its items from the work
+  // queue a.queue (see queue_claim).
   const int n_items = per_g * a.hkv;
-  const int qq = n_items >> 3, qr = n_items & 7;
-  const auto claim = [&]() -> int {  // (one thread)
-    const int x0 = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // XCC_ID
-    for (int d = 0; d < 8; ++d) {
-      const int x = (x0 + d) & 7;
-      const int size = qq + (x < qr ? 1 : 0);
-      if (size == 0) continue;
-      const int i = (int)atomicAdd(a.queue + x, 1u);
-      if (i < size) return (x < qr ? x * (qq + 1) : qr * (qq + 1) + (x - qr) * qq) + i;
-    }
-    return -1;
-  };
 
   // One work item (round k); thread 0 leaves the item it claims for the
   // next round in s_next[(k + 1) & 1].
@@ -261,7 +243,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   waitcnt<0, 15>();
   flash_walk_start(n_tiles, load_k, load_v);
   if constexpr (!SPLIT)
-    if (tid == 0) s_next[(k + 1) & 1] = claim();  // (its latency hides behind the walk)
+    if (tid == 0) s_next[(k + 1) & 1] = queue_claim(a.queue, n_items);
 
   // Q: rotate at position t, fold scale * log2(e), round once to bf16.
   bf16x8 qb[KS];
@@ -279,16 +261,34 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
         (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
         offsetof(PrefillArgs, freq) + offsetof(RopeFreq, rev));
     asm volatile("" : "+s"(frev));
+    using AT = AngleTable<D>;
+    // With several heads per token (64 tokens of 4 heads) the workgroup's tw
+    // positions go through an LDS table in V stages 1-3 (untouched until the
+    // walk's first requests): one cos / sin per (token, frequency) instead of
+    // one per row.  Uniform condition.
+    if (tw % 64 == 0 && tw * AT::ROWB <= 3 * Gm::VBYTES) {
+      char* const tab = vring + Gm::VBYTES;
+      AT::fill(tab, tw, tix, 64 * kPrefillWaves, [&](int j) -> int64_t { return r0 + j; },
+               [&](int f) { return (double)frev[f]; });
+      __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks) {
-      float c[8], sn[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        double f0 = frev[16 * ks + r], f1 = frev[16 * ks + 8 + r];
-        asm volatile("" : "+s"(f0), "+s"(f1));  // (kept as two scalar loads)
-        rope_cs(t, hh ? f1 : f0, c[r], sn[r]);
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        float c[8], sn[8];
+        AT::read8(tab, wrow + col, 16 * ks + 8 * hh, c, sn);
+        rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
       }
-      rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        float c[8], sn[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          double f0 = frev[16 * ks + r], f1 = frev[16 * ks + 8 + r];
+          asm volatile("" : "+s"(f0), "+s"(f1));  // (kept as two scalar loads)
+          rope_cs(t, hh ? f1 : f0, c[r], sn[r]);
+        }
+        rotate_chunk(raw[ks], raw[ks + KS / 2], c, sn, a.q_scale);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
@@ -361,20 +361,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
   }
   };
 
-  if constexpr (SPLIT) {
-    run(xcd_logical(blockIdx.x, gridDim.x), 0);
-  } else {
-    if (tid == 0) s_next[0] = claim();
-    __syncthreads();
-    for (int k = 0;; ++k) {
-      const int item = s_next[k & 1];
-      if (item < 0) break;
-      run(item, k);
-      // The next item, and (every wave has finished with the K ring, which
-      // held the output staging) free LDS for its first tile requests.
-      __syncthreads();
-    }
-  }
+  if constexpr (SPLIT) run(xcd_logical(blockIdx.x, gridDim.x), 0);
+  else queue_loop(a.queue, n_items, s_next, run);
 }
 
 // ---------------------------------------------------------------------------
