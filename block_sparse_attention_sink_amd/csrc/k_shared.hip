@@ -278,16 +278,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
       const int ch = (m * 4 + q4) ^ (col & (CPR - 1));
       *reinterpret_cast<u32x2*>(ost + col * Gm::ROW + ch * 16 + hh * 8) = w;
     }
-  // Destination of each staged row (the rows of one wave may span two pairs).
+  // Destination of each staged row: row rr_w of the wave belongs to lane
+  // rr_w, which has its (query, slot) pair in registers (the rows of one wave
+  // may span two pairs).
   constexpr int RPI = 64 / CPR;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave / RPI; ++i) {
     const int rr_w = i * RPI + lane / CPR, ch = lane % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(ost + rr_w * Gm::ROW + (ch ^ (rr_w & (CPR - 1))) * 16);
     const int rho_s = chunk * kPrefillRows + wave * kRowsPerWave + rr_w;
+    const int qi_s = __shfl(qi, rr_w);
     if (rho_s < n_rows) {
       const int pr_s = rho_s / a.rq;
-      const int qi_s = tb.pairs[2 * (p0 + pr_s)];
       const int64_t row = (((int64_t)(qi_s >> 16) * a.hkv + g) * a.n_ids + (qi_s & 0xffff)) * a.rq +
                           (rho_s - pr_s * a.rq);
       *reinterpret_cast<u32x4*>(a.part_o + row * D + ch * 8) = v;
