@@ -125,16 +125,16 @@ size_t elem_bytes(const dbsa_attn_t* a) { return a->dtype == DBSA_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
 // Per-call tables that do not fit the kernel arguments: written into the
-// workspace by k_upload launches on the caller's stream (kInlineInts ints per
+// workspace by k_upload launches on the caller's stream (kUploadInts ints per
 // launch).  Nothing is staged in host memory and the host never waits.
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxTableBytes = size_t(1) << 20;
 
 int upload_ints(const int32_t* src, size_t n, void* dst, hipStream_t s) {
-  for (size_t i = 0; i < n; i += kInlineInts) {
+  for (size_t i = 0; i < n; i += kUploadInts) {
     UploadArgs ua;
     ua.dst = static_cast<int32_t*>(dst) + i;
-    ua.n = (int32_t)std::min<size_t>(kInlineInts, n - i);
+    ua.n = (int32_t)std::min<size_t>(kUploadInts, n - i);
     std::memcpy(ua.v, src + i, (size_t)ua.n * sizeof(int32_t));
     const hipError_t e = launch_upload(ua, s);
     if (e != hipSuccess) return hip_fail(e, "launch upload");

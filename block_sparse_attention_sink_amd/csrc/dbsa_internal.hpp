@@ -55,10 +55,14 @@ struct PackArgs {
 // is ordered on the caller's stream and needs no host staging memory.
 constexpr int kInlineInts = 512;
 
+// One k_upload launch carries up to kUploadInts ints (the argument block
+// stays under 4 KiB).  Its duration is mostly the latency of reading the
+// argument block, so fewer, larger launches are faster.
+constexpr int kUploadInts = 960;
 struct UploadArgs {
   int32_t* dst;
   int32_t n;
-  int32_t v[kInlineInts];
+  int32_t v[kUploadInts];
 };
 
 struct PrefillArgs {

@@ -1,7 +1,7 @@
 // Upload of small int32 tables (block offsets, segment lists) into device
 // memory, ordered on the caller's stream: the values ride in the kernel
 // arguments of k_upload, so no host staging memory and no host wait is
-// involved.  A table of n ints takes ceil(n / kInlineInts) launches.
+// involved.  A table of n ints takes ceil(n / kUploadInts) launches.
 #include "dbsa_device.hpp"
 
 namespace dbsa {

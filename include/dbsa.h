@@ -33,7 +33,7 @@
  *    workspace must not be shared by calls that may overlap.
  *  - Per-call tables built from the host arrays (block offsets, segment
  *    lists) travel in the kernel arguments when they fit (512 int32), else
- *    they are written into the workspace by small copy kernels, 512 int32 per
+ *    they are written into the workspace by small copy kernels, 960 int32 per
  *    launch, on `stream`.  The host never waits and nothing is staged in host
  *    memory.  Tables above 1 MiB are DBSA_EUNSUPPORTED.
  *  - Calls are thread-safe; error text is thread-local.
