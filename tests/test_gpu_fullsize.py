@@ -96,7 +96,7 @@ def test_stress_patterns_full_size(pattern):
     q, k, v = _qkv(w, 500)
     o = dbsa.dbsa_prefill(q, k, v, w.block_lens, sink, j, w.theta)
     torch.cuda.synchronize()
-    rows = _sample_rows(w.block_lens, j, per_edge=4, n_random=8, seed=5)
+    rows = _sample_rows(w.block_lens, j, per_edge=8, n_random=40, seed=5)
     _check_prefill_rows(w, q, k, v, o, sink, j, rows, f"stress {pattern}")
 
 
