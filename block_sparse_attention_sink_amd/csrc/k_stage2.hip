@@ -773,11 +773,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // the tail / new-token pass (unnormalised O, m, l):
 //   O = (sum_i 2^(lambda_i - M) O_i + sum_s 2^(m_s - M) O_s)
 //       / (sum_i 2^(lambda_i - M) + sum_s 2^(m_s - M) l_s),
-// M the largest exponent among them.  16 threads per row, 8 head dims each.
+// M the largest exponent among them.  16 threads per row, 8 head dims each;
+// the block partials are read once, 8 at a time, past the caches (8 in
+// flight instead of 4: 163 -> 143 us on the 32-layer pool batch).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR, U = 4;
+  constexpr int TPR = D / 8, RPB = 256 / TPR, U = 8;
   const int rho = blockIdx.x * RPB + threadIdx.x / TPR, c = threadIdx.x % TPR;
   const int g = blockIdx.y, b = blockIdx.z;
   if (rho >= a.rq) return;
@@ -809,7 +811,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
       const int i = min(i0 + u, a.n_ids - 1);
       const int64_t row = (pb + i) * a.rq + rho;
       lam[u] = i0 + u < a.n_ids ? a.part_lam[row] : kNegInf;
-      xs[u] = *reinterpret_cast<const u32x4*>(a.part_o + row * D + 8 * c);
+      xs[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + row * D + 8 * c));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
