@@ -123,11 +123,23 @@ def stage2_work(lens, ids, n_new, hq, hkv, d, esz=2):
 # ---------------------------------------------------------------------------
 # Profile summaries (HBM traffic per launch, if taken on the current sources)
 # ---------------------------------------------------------------------------
+def _code_only(text):
+    """C++ source with comments and blank lines removed, lines right-stripped:
+    an edit to a comment leaves the kernel, and so its counters, unchanged.
+    (The kernel sources hold no string literal that contains a comment
+    marker.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_digest(paths):
-    """sha256 over the concatenated bytes of the kernel's source files."""
+    """sha256 over the code of the kernel's source files (comments left out),
+    concatenated in order."""
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        h.update(_code_only(open(p).read()).encode())
+        h.update(b"\n")
     return h.hexdigest()
 
 

@@ -3,8 +3,8 @@
 // [Notes, Method > Stage 1]: block i attends to the anchor block (sink), to the
 // previous j blocks and causally to itself; tokens sit at sequential
 // positions; K/V are kept unrotated.  The page's implementation skips masked
-// blocks; here the skipping is by construction: each 128-row query tile walks
-// only the 64-key tiles that meet its visible key intervals.
+// blocks; here the skipping is by construction: each query tile walks only
+// the 64-key tiles that meet its visible key intervals.
 //
 // Kernels
 //   k_pack_bf16     rotate K once per key tile and transpose V, writing each
@@ -48,8 +48,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_pack_bf16(PackArgs a) {
 // ---------------------------------------------------------------------------
 // Block-sparse flash prefill, bf16 in / bf16 out, fp32 accumulation.
 //
-// Workgroup = 8 wavefronts = 256 query rows of one query head; wave w owns
-// rows r0 + 32w .. +31 (lane layout: see Flash).  The workgroup walks the
+// Workgroup = 8 wavefronts = 256 query rows (256 / P tokens x P query heads
+// of one KV head, below); each wave owns 32 rows (lane layout: see Flash).  The workgroup walks the
 // 64-key tiles that meet its rows' visible intervals.  K tiles and V tiles
 // have separate LDS rings of 4 stages, filled by direct global->LDS loads
 // two tiles at a time (see the loop).
