@@ -330,16 +330,19 @@ struct Flash {
                                                           o[j % OT], 0, 0, 0);
   }
 
+  struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+  };
   // Mask (when `mask`: key kr of the tile is kept iff vis(kr)), row maximum
   // and the rare reference raise (rescaling o and l); leaves s = S - m.  When
   // PV, the previous tile's O^T += V^T P^T (V from st_v, probabilities p) is
-  // issued in 16 groups, fenced against the scheduler: group j holds P V
-  // product j (its fragments were read two groups earlier) and one step of
-  // the maximum tree.
-  template <bool PV, typename Vis>
+  // issued in NPV groups, fenced against the scheduler: group j holds P V
+  // product j (its fragments were read two groups earlier), one step of the
+  // maximum tree and hook(j) (the caller's tile requests, if any).
+  template <bool PV, typename Vis, typename Hook = NoHook>
   __device__ __forceinline__ void pv_head(const char* st_v, const int (&vbase)[OT],
                                           const bf16x8 (&p)[4], f32x16& s0, f32x16& s1, bool mask,
-                                          Vis vis) {
+                                          Vis vis, Hook hook = Hook{}) {
     if (mask) {
       keep_branch();
       const int hh = (threadIdx.x >> 5) & 1;
@@ -376,6 +379,7 @@ struct Flash {
         if (j + 2 < NPV) va[(j + 2) % 3] = vfrag(st_v, vbase, j + 2);
         o[j % OT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j % 3], p[j / OT], o[j % OT], 0, 0, 0);
         max_step(j);
+        hook(j);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
@@ -610,7 +614,11 @@ __device__ __forceinline__ void barrier_nofence() {
 // (each wave waits for its own, the barrier for all), and the stages of K
 // tiles i - 1, i and V tiles i - 3, i - 2 are refilled for the next two
 // iterations; odd iterations run without one, so the two wavefronts of a SIMD
-// can drift apart.  The loop is unrolled over the four stages: every LDS
+// can drift apart.  The refill requests go out in four parts spread over the
+// P V group of the even iteration: issued together right after the barrier,
+// the 64 direct loads of a workgroup queued at the memory unit and every wave
+// waited there (about 15% of the walk, measured), the two waves of a SIMD at
+// the same time.  The loop is unrolled over the four stages: every LDS
 // fragment address is then the lane's base plus a constant, and the score
 // registers alternate instead of being copied.  The last iteration also
 // computes scores of a stale K stage; they are never used.  Leaves O, m, l
@@ -643,6 +651,25 @@ __device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char
     barrier_nofence();
     request(i);
   };
+  const auto sync_only = [&]() {
+    wait_vm(0);
+    barrier_nofence();
+  };
+  // The requests of even iteration i, one part every quarter of its P V group.
+  constexpr int ST = Flash<D>::NPV / 4;
+  const auto spread_request = [&](int i) {
+    return [&, i](int j) {
+      if (j == 0) {
+        if (i + 3 < n_tiles) load_k(i + 3);
+      } else if (j == ST) {
+        if (i + 4 < n_tiles) load_k(i + 4);
+      } else if (j == 2 * ST) {
+        if (i + 1 < n_tiles) load_v(i + 1);
+      } else if (j == 3 * ST) {
+        if (i + 2 < n_tiles) load_v(i + 2);
+      }
+    };
+  };
   const auto ks = [&](int st) { return kring + st * Gm::KBYTES; };
   const auto vs = [&](int st) { return vring + st * Gm::VBYTES; };
   // Prologue: K of tiles 0, 1, 2 and V of tile 0 (issued by
@@ -659,15 +686,17 @@ __device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char
     fl.template pv_head<true>(vs(0), vbase, pr, n0, n1, !full_of(i), vis_of(i));
     fl.exp_next(ks(2), koff, qb, n0, n1, pr, s0, s1);
     if (i + 1 >= n_tiles) break;
-    sync(i + 1);
-    fl.template pv_head<true>(vs(1), vbase, pr, s0, s1, !full_of(i + 1), vis_of(i + 1));
+    sync_only();
+    fl.template pv_head<true>(vs(1), vbase, pr, s0, s1, !full_of(i + 1), vis_of(i + 1),
+                              spread_request(i + 1));
     fl.exp_next(ks(3), koff, qb, s0, s1, pr, n0, n1);
     if (i + 2 >= n_tiles) break;
     fl.template pv_head<true>(vs(2), vbase, pr, n0, n1, !full_of(i + 2), vis_of(i + 2));
     fl.exp_next(ks(0), koff, qb, n0, n1, pr, s0, s1);
     if (i + 3 >= n_tiles) break;
-    sync(i + 3);
-    fl.template pv_head<true>(vs(3), vbase, pr, s0, s1, !full_of(i + 3), vis_of(i + 3));
+    sync_only();
+    fl.template pv_head<true>(vs(3), vbase, pr, s0, s1, !full_of(i + 3), vis_of(i + 3),
+                              spread_request(i + 3));
     fl.exp_next(ks(1), koff, qb, s0, s1, pr, n0, n1);
   }
   // P V of the last tile (its V may have been requested by the last barrier).
