@@ -609,7 +609,9 @@ __device__ __forceinline__ void barrier_nofence() {
 // of four stages (tile t in stage t % 4), filled by the caller's load_k /
 // load_v (direct global -> LDS loads, two tiles at a time).  Iteration i
 // computes the softmax of tile i, P V of tile i - 1 and the scores of tile
-// i + 1 (reading K of tile i + 1, V of tile i - 1).  Even iterations start
+// i + 1 (reading K of tile i + 1, V of tile i - 1).  V fragments are read at
+// vread + stage * VBYTES + vbase[..]: the kernels pass the start of their LDS
+// block and keep the V ring's offset in vbase.  Even iterations start
 // with a barrier: every load requested two iterations earlier has landed
 // (each wave waits for its own, the barrier for all), and the stages of K
 // tiles i - 1, i and V tiles i - 3, i - 2 are refilled for the next two
@@ -633,7 +635,7 @@ __device__ __forceinline__ void flash_walk_start(const int n_tiles, LoadK&& load
 }
 
 template <int D, typename LoadK, typename LoadV, typename FullOf, typename VisOf>
-__device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char* const vring,
+__device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char* const vread,
                                            const int n_tiles, const int (&koff)[D / 16],
                                            const int (&vbase)[D / 32],
                                            const bf16x8 (&qb)[D / 16], LoadK&& load_k,
@@ -671,7 +673,7 @@ __device__ __forceinline__ void flash_walk(Flash<D>& fl, char* const kring, char
     };
   };
   const auto ks = [&](int st) { return kring + st * Gm::KBYTES; };
-  const auto vs = [&](int st) { return vring + st * Gm::VBYTES; };
+  const auto vs = [&](int st) { return vread + st * Gm::VBYTES; };
   // Prologue: K of tiles 0, 1, 2 and V of tile 0 (issued by
   // flash_walk_start), all landed before the scores of tile 0.
   wait_vm(0);

@@ -250,6 +250,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
 
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
+  // The V ring's offset goes into the lane's bases, and the walk addresses V
+  // fragments from the start of the LDS block: every V read then takes its
+  // stage and step as an immediate offset (the ring starts 64 KiB in, past
+  // the reach of that offset field, and the address additions would
+  // otherwise be redone every tile).
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    vbase[t] += static_cast<int>(vring - lds);
+    asm volatile("" : "+v"(vbase[t]));
+  }
 
   // Every row sees the whole block: only its last tile, which may reach
   // past it, needs the element mask.
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_shared_bf16(SharedArg
     const int hi = key1 - (key0 + it * kKeyTile);
     return [=](int kr) { return kr < hi; };
   };
-  flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb8, load_k, load_v, full_of, vis_of);
+  flash_walk<D>(fl, kring, lds, n_tiles, koff, vbase, qb8, load_k, load_v, full_of, vis_of);
 
   // O / l in bf16 and lambda = m + log2(l), staged row by row through the
   // wave's part of the (idle) K ring so whole 16-byte chunks go out.

@@ -299,6 +299,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
 
   int koff[KS], vbase[D / 32];
   lane_offsets<D>(lane, koff, vbase);
+  // The V ring's offset goes into the lane's bases, and the walk addresses V
+  // fragments from the start of the LDS block: every V read then takes its
+  // stage and step as an immediate offset (the ring starts 64 KiB in, past
+  // the reach of that offset field, and the address additions would
+  // otherwise be redone every tile).
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    vbase[t] += static_cast<int>(vring - lds);
+    asm volatile("" : "+v"(vbase[t]));
+  }
 
   // Element mask only on tiles some row cannot fully see.
   const auto full_of = [&](int it) {
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_prefill_bf16(PrefillA
     const int tt = t - k0, lt = lo_t - k0, se = sink_end - k0;
     return [=](int kr) { return kr <= tt && (kr >= lt || kr < se); };
   };
-  flash_walk<D>(fl, kring, vring, n_tiles, koff, vbase, qb, load_k, load_v, full_of, vis_of);
+  flash_walk<D>(fl, kring, lds, n_tiles, koff, vbase, qb, load_k, load_v, full_of, vis_of);
 
   const float lsum = fl.total();
   if constexpr (SPLIT) {
